@@ -1,0 +1,252 @@
+"""CPU oracle for the quantized linear layer (TEST INFRASTRUCTURE).
+
+Only ``tests/``, ``__graft_entry__.smoke()`` and ``bench.py``'s CPU-baseline
+leg may import this package. It wraps ``liboracle.so`` (plain single-threaded
+C++ built from ``oracle.cpp`` with g++ -O2 -ffp-contract=off) through ctypes
+and composes its steps in the order the pages give them:
+
+  1. optional block Walsh-Hadamard rotation (HQ-DM, technical summary 2.1),
+  2. DualScale per-tensor act scales and codes (SegQuant, section 2.B),
+  3. optional LSB truncation of the codes (TASQ, section 2),
+  4. weight scales per channel / output segment / tensor (SegQuant, 2.A),
+  5. the two integer contractions and the fp32 epilogue (SegQuant, 2.B),
+  6. the classifier-free-guidance combine (Closing the Null Space, problem
+     statement).
+
+It shares no code with the GPU library and never calls it.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+from typing import Optional, Sequence
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "oracle.cpp")
+_LIB = os.path.join(_HERE, "liboracle.so")
+
+DUAL, SYMMETRIC = 0, 1
+W_TENSOR, W_SEGMENT, W_CHANNEL = 0, 1, 2
+_WMODES = {"tensor": W_TENSOR, "segment": W_SEGMENT, "channel": W_CHANNEL}
+_AMODES = {"dual": DUAL, "symmetric": SYMMETRIC}
+
+
+def build(force: bool = True) -> str:
+    """Compile liboracle.so with the host compiler (plain C++17)."""
+    if not force and os.path.exists(_LIB):
+        return _LIB
+    cmd = ["g++", "-std=c++17", "-O2", "-ffp-contract=off", "-fno-fast-math",
+           "-fPIC", "-shared", "-Wall", "-Wextra", "-o", _LIB + ".tmp", _SRC]
+    subprocess.run(cmd, check=True)
+    os.replace(_LIB + ".tmp", _LIB)
+    return _LIB
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB):
+            build(force=False)
+        L = ctypes.CDLL(_LIB)
+        P = ctypes.c_void_p
+        I32, I64, F32 = ctypes.c_int32, ctypes.c_int64, ctypes.c_float
+        sigs = {
+            "orc_fwht_block": [P, I32],
+            "orc_rotate_rows": [P, I64, I64, I32],
+            "orc_act_scales": [P, I64, I32, I32, P],
+            "orc_quant_value": [F32, F32, F32, I32],
+            "orc_truncate_lsb": [I32, I32],
+            "orc_quantize_act": [P, I64, P, I32, I32, P],
+            "orc_pack_int4": [P, I64, I64, P],
+            "orc_unpack_int4": [P, I64, I64, P],
+            "orc_weight_scales": [P, I64, I64, I32, I32, I32, P, P],
+            "orc_quantize_weight": [P, I64, I64, P, I32, P],
+            "orc_gemm_dual": [P, P, P, I64, I64, I64, P, P],
+            "orc_epilogue": [P, P, I64, I64, P, P, I32, I32, P],
+            "orc_cfg_combine": [P, P, I64, I64, F32, P],
+            "orc_bf16_to_f32": [P, I64, P],
+        }
+        for name, args in sigs.items():
+            fn = getattr(L, name)
+            fn.argtypes = args
+            fn.restype = I32
+        _lib = L
+    return _lib
+
+
+class OracleError(RuntimeError):
+    pass
+
+
+def _ck(rc: int, what: str):
+    if rc != 0:
+        raise OracleError(f"{what} failed with oracle code {rc}")
+
+
+def _p(a: Optional[np.ndarray]):
+    return None if a is None else a.ctypes.data_as(ctypes.c_void_p)
+
+
+def qmax(bits: int) -> int:
+    return (1 << (bits - 1)) - 1
+
+
+# ----------------------------------------------------------------- steps ----
+
+def fwht_block(v: np.ndarray) -> np.ndarray:
+    out = np.array(v, dtype=np.float32, copy=True)
+    _ck(lib().orc_fwht_block(_p(out), out.size), "fwht_block")
+    return out
+
+
+def rotate(x: np.ndarray, B: int) -> np.ndarray:
+    """Rows of x [rows, K] rotated block-wise by the unnormalised H_B (copy)."""
+    out = np.array(x, dtype=np.float32, copy=True, order="C")
+    rows, K = out.shape
+    _ck(lib().orc_rotate_rows(_p(out), rows, K, B), "rotate_rows")
+    return out
+
+
+def bf16_to_f32(bits: np.ndarray) -> np.ndarray:
+    b = np.ascontiguousarray(bits, dtype=np.uint16)
+    out = np.empty(b.shape, dtype=np.float32)
+    _ck(lib().orc_bf16_to_f32(_p(b), b.size, _p(out)), "bf16_to_f32")
+    return out
+
+
+def act_scales(x: np.ndarray, a_bits: int, mode: str = "dual") -> np.ndarray:
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    s = np.zeros(2, dtype=np.float32)
+    _ck(lib().orc_act_scales(_p(x), x.size, a_bits, _AMODES[mode], _p(s)), "act_scales")
+    return s
+
+
+def quant_value(v: float, sp: float, sn: float, bits: int) -> int:
+    return int(lib().orc_quant_value(v, sp, sn, qmax(bits)))
+
+
+def truncate_lsb(c: int, k: int) -> int:
+    return int(lib().orc_truncate_lsb(int(c), int(k)))
+
+
+def quantize_act(x: np.ndarray, s: np.ndarray, a_bits: int, lsb_k: int = 0) -> np.ndarray:
+    """Signed codes (int8, unpacked) for fp32 x with scales s = (s+, s-)."""
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    s = np.ascontiguousarray(s, dtype=np.float32)
+    c = np.empty(x.shape, dtype=np.int8)
+    _ck(lib().orc_quantize_act(_p(x), x.size, _p(s), a_bits, lsb_k, _p(c)), "quantize_act")
+    return c
+
+
+def pack_int4(codes: np.ndarray) -> np.ndarray:
+    codes = np.ascontiguousarray(codes, dtype=np.int8)
+    rows, K = codes.shape
+    out = np.empty((rows, K // 2), dtype=np.uint8)
+    _ck(lib().orc_pack_int4(_p(codes), rows, K, _p(out)), "pack_int4")
+    return out
+
+
+def unpack_int4(packed: np.ndarray, K: int) -> np.ndarray:
+    packed = np.ascontiguousarray(packed, dtype=np.uint8)
+    rows = packed.shape[0]
+    out = np.empty((rows, K), dtype=np.int8)
+    _ck(lib().orc_unpack_int4(_p(packed), rows, K, _p(out)), "unpack_int4")
+    return out
+
+
+def weight_scales(w: np.ndarray, w_bits: int, mode: str = "channel",
+                  seg_offsets: Optional[Sequence[int]] = None) -> np.ndarray:
+    w = np.ascontiguousarray(w, dtype=np.float32)
+    N, K = w.shape
+    sw = np.empty(N, dtype=np.float32)
+    seg = None if seg_offsets is None else np.ascontiguousarray(seg_offsets, dtype=np.int32)
+    nseg = 1 if seg is None else seg.size - 1
+    _ck(lib().orc_weight_scales(_p(w), N, K, w_bits, _WMODES[mode], nseg, _p(seg), _p(sw)),
+        "weight_scales")
+    return sw
+
+
+def quantize_weight(w: np.ndarray, sw: np.ndarray, w_bits: int) -> np.ndarray:
+    w = np.ascontiguousarray(w, dtype=np.float32)
+    sw = np.ascontiguousarray(sw, dtype=np.float32)
+    N, K = w.shape
+    wc = np.empty((N, K), dtype=np.int8)
+    _ck(lib().orc_quantize_weight(_p(w), N, K, _p(sw), w_bits, _p(wc)), "quantize_weight")
+    return wc
+
+
+def gemm_dual(codes: np.ndarray, wc: np.ndarray, rows: Optional[Sequence[int]] = None):
+    """(acc+, acc-) int32 [len(rows), N] for the listed rows of codes [M,K]."""
+    codes = np.ascontiguousarray(codes, dtype=np.int8)
+    wc = np.ascontiguousarray(wc, dtype=np.int8)
+    M, K = codes.shape
+    N = wc.shape[0]
+    assert wc.shape[1] == K
+    r = np.arange(M, dtype=np.int64) if rows is None else np.ascontiguousarray(rows, dtype=np.int64)
+    accp = np.empty((r.size, N), dtype=np.int32)
+    accn = np.empty((r.size, N), dtype=np.int32)
+    _ck(lib().orc_gemm_dual(_p(codes), _p(wc), _p(r), r.size, N, K, _p(accp), _p(accn)),
+        "gemm_dual")
+    return accp, accn
+
+
+def epilogue(accp: np.ndarray, accn: np.ndarray, s: np.ndarray, sw: np.ndarray,
+             B: int = 0, mode: str = "dual") -> np.ndarray:
+    accp = np.ascontiguousarray(accp, dtype=np.int32)
+    accn = np.ascontiguousarray(accn, dtype=np.int32)
+    s = np.ascontiguousarray(s, dtype=np.float32)
+    sw = np.ascontiguousarray(sw, dtype=np.float32)
+    rows, N = accp.shape
+    y = np.empty((rows, N), dtype=np.float32)
+    _ck(lib().orc_epilogue(_p(accp), _p(accn), rows, N, _p(s), _p(sw), B, _AMODES[mode], _p(y)),
+        "epilogue")
+    return y
+
+
+def cfg_combine(y_c: np.ndarray, y_u: np.ndarray, w: float) -> np.ndarray:
+    y_c = np.ascontiguousarray(y_c, dtype=np.float32)
+    y_u = np.ascontiguousarray(y_u, dtype=np.float32)
+    assert y_c.shape == y_u.shape
+    rows, N = y_c.shape
+    out = np.empty_like(y_c)
+    _ck(lib().orc_cfg_combine(_p(y_c), _p(y_u), rows, N, float(w), _p(out)), "cfg_combine")
+    return out
+
+
+# --------------------------------------------------------------- pipeline ----
+
+class WeightPlan:
+    """Oracle weights for one linear: codes int8 [N,K] and scales [N]."""
+
+    def __init__(self, W: np.ndarray, w_bits: int, B: int = 0, mode: str = "channel",
+                 seg_offsets: Optional[Sequence[int]] = None):
+        Wr = rotate(W, B) if B else np.ascontiguousarray(W, dtype=np.float32)
+        self.w_bits, self.B = w_bits, B
+        self.scales = weight_scales(Wr, w_bits, mode, seg_offsets)
+        self.codes = quantize_weight(Wr, self.scales, w_bits)
+
+
+def quantize_activations(X: np.ndarray, a_bits: int, B: int = 0, mode: str = "dual",
+                         lsb_k: int = 0, static_scales: Optional[np.ndarray] = None,
+                         bf16: bool = False):
+    """Rotate (optional), take per-tensor scales (or the given static ones),
+    quantize and truncate. Returns (codes int8 [M,K], scales [2])."""
+    x = bf16_to_f32(X) if bf16 else np.ascontiguousarray(X, dtype=np.float32)
+    if B:
+        x = rotate(x, B)
+    s = (act_scales(x, a_bits, mode) if static_scales is None
+         else np.ascontiguousarray(static_scales, dtype=np.float32).copy())
+    return quantize_act(x, s, a_bits, lsb_k), s
+
+
+def linear_rows(codes: np.ndarray, s: np.ndarray, wp: WeightPlan, rows: Sequence[int],
+                mode: str = "dual"):
+    """Epilogue outputs y [len(rows), N] plus the accumulators for those rows."""
+    accp, accn = gemm_dual(codes, wp.codes, rows)
+    return epilogue(accp, accn, s, wp.scales, wp.B, mode), accp, accn

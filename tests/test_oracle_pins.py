@@ -1,0 +1,434 @@
+"""Pins for the CPU oracle: closed forms, invariants, library special cases,
+hand-derived fixtures and brute force. None of these re-types the oracle's
+own formulas; each is chosen so that a plausible slip (dropped term, wrong
+sign, swapped scale, transposed operand, wrong rounding) fails one of them.
+"""
+import json
+import os
+
+import numpy as np
+import pytest
+import scipy.linalg
+
+from workloads import synth
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _golden(name):
+    with open(os.path.join(GOLDEN, name)) as f:
+        return json.load(f)
+
+
+# ------------------------------------------------------------------ P1 FWHT --
+
+def test_fwht_golden_block8(orc):
+    g = _golden("hadamard8.json")
+    out = orc.fwht_block(np.array(g["x"], np.float32))
+    assert out.tolist() == g["Hx"]
+
+
+@pytest.mark.parametrize("B", [2, 4, 8, 16, 32, 64, 128, 256])
+def test_fwht_equals_sylvester_matrix_exactly(orc, B):
+    # scipy.linalg.hadamard builds the Sylvester-ordered matrix. Integer inputs
+    # with |sums| < 2^24 make every fp32 butterfly exact.
+    H = scipy.linalg.hadamard(B).astype(np.int64)
+    rng = np.random.default_rng(B)
+    for _ in range(4):
+        x = rng.integers(-1000, 1000, size=B)
+        out = orc.fwht_block(x.astype(np.float32))
+        assert np.array_equal(out.astype(np.int64), H @ x)
+
+
+@pytest.mark.parametrize("B", [4, 16, 128])
+def test_fwht_involution_and_orthogonality(orc, B):
+    H = scipy.linalg.hadamard(B).astype(np.int64)
+    assert np.array_equal(H @ H.T, B * np.eye(B, dtype=np.int64))
+    x = np.arange(-B // 2, B // 2, dtype=np.float32)
+    twice = orc.fwht_block(orc.fwht_block(x))
+    assert np.array_equal(twice, B * x)
+
+
+def test_rotate_rows_is_block_diagonal(orc):
+    B, K, rows = 8, 32, 3
+    rng = np.random.default_rng(1)
+    x = rng.integers(-50, 50, size=(rows, K))
+    Hbd = np.kron(np.eye(K // B, dtype=np.int64), scipy.linalg.hadamard(B).astype(np.int64))
+    out = orc.rotate(x.astype(np.float32), B)
+    assert np.array_equal(out.astype(np.int64), x @ Hbd.T)
+
+
+def test_rotation_preserves_product(orc):
+    # (1/B) (X H)(W H)^T = X W^T: the normalisation folded as 1/B.
+    B = 128
+    rng = np.random.default_rng(2)
+    X = rng.integers(-8, 8, size=(5, 256)).astype(np.float32)
+    W = rng.integers(-8, 8, size=(7, 256)).astype(np.float32)
+    Xr = orc.rotate(X, B).astype(np.float64)
+    Wr = orc.rotate(W, B).astype(np.float64)
+    lhs = (Xr @ Wr.T) / B
+    rhs = X.astype(np.float64) @ W.astype(np.float64).T
+    assert np.array_equal(lhs, rhs)
+
+
+def test_rotate_rejects_bad_block(orc):
+    with pytest.raises(orc.OracleError):
+        orc.rotate(np.zeros((2, 24), np.float32), 16)
+    with pytest.raises(orc.OracleError):
+        orc.rotate(np.zeros((2, 24), np.float32), 12)
+
+
+# ------------------------------------------------------- golden end to end --
+
+def test_golden_dualscale_cfg(orc):
+    g = _golden("dualscale_cfg_2x4.json")
+    X = np.array(g["X"], np.float32)
+    W = np.array(g["W"], np.float32)
+    codes, s = orc.quantize_activations(X, g["a_bits"])
+    assert s.tolist() == g["act_scales"]
+    assert codes.tolist() == g["codes"]
+    wp = orc.WeightPlan(W, g["w_bits"])
+    assert wp.scales.tolist() == g["w_scales"]
+    assert wp.codes.tolist() == g["w_codes"]
+    y, accp, accn = orc.linear_rows(codes, s, wp, [0, 1])
+    assert accp.tolist() == g["acc_plus"]
+    assert accn.tolist() == g["acc_minus"]
+    assert y.tolist() == g["y"]
+    out = orc.cfg_combine(y[:1], y[1:], g["guidance"])
+    assert out.tolist() == g["cfg_out"]
+
+
+# -------------------------------------------------------------- P2 scales --
+
+@pytest.mark.parametrize("bits", [8, 4])
+def test_scales_extremes_map_to_qmax(orc, bits):
+    x = synth.silu_normal(3, "t/p2", 64, 96)
+    s = orc.act_scales(x, bits)
+    q = orc.qmax(bits)
+    c = orc.quantize_act(x, s, bits)
+    assert c.reshape(-1)[np.argmax(x)] == q
+    assert c.reshape(-1)[np.argmin(x)] == -q
+    assert c.max() == q and c.min() == -q
+    # s+ and s- differ for an asymmetric (SiLU) tensor: a swapped pair would
+    # put the negative extreme far from -q.
+    assert s[0] > 10 * s[1]
+
+
+def test_scales_degenerate_regions(orc):
+    pos = np.abs(synth.silu_normal(4, "t/pos", 8, 8)) + 0.1
+    s = orc.act_scales(pos, 8)
+    assert s[1] == 0.0 and s[0] > 0
+    c = orc.quantize_act(-pos, orc.act_scales(-pos, 8), 8)
+    assert (c <= 0).all() and c.min() == -127
+    z = np.zeros((4, 4), np.float32)
+    z[0, 0] = -0.0
+    s0 = orc.act_scales(z, 8)
+    assert s0.tolist() == [0.0, 0.0] and not np.signbit(s0).any()
+    assert (orc.quantize_act(z, s0, 8) == 0).all()
+
+
+def test_scales_reject_nonfinite(orc):
+    x = np.ones((2, 2), np.float32)
+    x[1, 1] = np.inf
+    with pytest.raises(orc.OracleError):
+        orc.act_scales(x, 8)
+    x[1, 1] = np.nan
+    with pytest.raises(orc.OracleError):
+        orc.quantize_act(x, np.array([1, 1], np.float32), 8)
+
+
+# --------------------------------------------------- P3 dual -> symmetric --
+
+@pytest.mark.parametrize("bits", [8, 4])
+def test_equal_scales_reduce_to_symmetric(orc, bits):
+    x = synth.gelu_normal(5, "t/p3", 33, 70)
+    q = orc.qmax(bits)
+    s_sym = orc.act_scales(x, bits, "symmetric")
+    assert s_sym[0] == s_sym[1]
+    c = orc.quantize_act(x, s_sym, bits)
+    # numpy: IEEE fp32 division and round-half-even, then clip.
+    ref = np.clip(np.rint(x / s_sym[0]), -q, q).astype(np.int8)
+    assert np.array_equal(c, ref)
+    W = synth.weight_normal(5, "t/p3w", 9, 70)
+    wp = orc.WeightPlan(W, 8)
+    accp, accn = orc.gemm_dual(c, wp.codes)
+    acc_sym = c.astype(np.int64) @ wp.codes.astype(np.int64).T
+    assert np.array_equal(accp.astype(np.int64) + accn, acc_sym)
+
+
+def test_weight_codes_match_numpy_symmetric(orc):
+    W = synth.weight_normal(6, "t/wq", 17, 40)
+    for bits in (8, 4):
+        q = orc.qmax(bits)
+        sw = orc.weight_scales(W, bits, "channel")
+        wc = orc.quantize_weight(W, sw, bits)
+        ref = np.clip(np.rint(W / sw[:, None]), -q, q).astype(np.int8)
+        assert np.array_equal(wc, ref)
+        # absmax row element hits +-q
+        am = np.argmax(np.abs(W), axis=1)
+        assert (np.abs(wc[np.arange(17), am]) == q).all()
+
+
+# ------------------------------------------------------ P4 error bound ------
+
+@pytest.mark.parametrize("bits", [8, 4])
+def test_quantization_error_bound(orc, bits):
+    x = synth.gelu_with_outliers(7, "t/p4", 64, 1152)
+    s = orc.act_scales(x, bits)
+    c = orc.quantize_act(x, s, bits).astype(np.float64)
+    sel = np.where(x >= 0, s[0], s[1]).astype(np.float64)
+    err = np.abs(x.astype(np.float64) - sel * c)
+    assert (err <= sel / 2 * (1 + 2.0 ** -22)).all()
+
+
+# ------------------------------------------------------ P5 monotonicity ------
+
+def test_codes_monotone(orc):
+    x = np.sort(synth.silu_normal(8, "t/p5", 1, 5000).reshape(-1))
+    s = orc.act_scales(x, 8)
+    c = orc.quantize_act(x, s, 8).astype(np.int32)
+    assert (np.diff(c) >= 0).all()
+    c4 = orc.quantize_act(x, orc.act_scales(x, 4), 4).astype(np.int32)
+    assert (np.diff(c4) >= 0).all() and c4.min() == -7 and c4.max() == 7
+
+
+# -------------------------------------------------------- P6 segments -------
+
+def test_segments_special_cases(orc):
+    W = synth.weight_normal(9, "t/p6", 24, 16)
+    for bits in (8, 4):
+        per_t = orc.weight_scales(W, bits, "tensor")
+        one = orc.weight_scales(W, bits, "segment", [0, 24])
+        assert np.array_equal(per_t, one)
+        assert (per_t == per_t[0]).all()
+        assert per_t[0] == np.float32(np.abs(W).max()) / np.float32(orc.qmax(bits))
+        per_c = orc.weight_scales(W, bits, "channel")
+        width1 = orc.weight_scales(W, bits, "segment", list(range(25)))
+        assert np.array_equal(per_c, width1)
+        seg = [0, 6, 12, 24]
+        per_s = orc.weight_scales(W, bits, "segment", seg)
+        for g in range(3):
+            blk = per_s[seg[g]:seg[g + 1]]
+            assert (blk == blk[0]).all()
+            # monotone rounding: max of per-channel scales == segment scale
+            assert blk[0] == per_c[seg[g]:seg[g + 1]].max()
+
+
+def test_segments_reject_bad_offsets(orc):
+    W = np.ones((8, 4), np.float32)
+    for bad in ([0, 4], [1, 8], [0, 4, 4, 8], [0, 6, 3, 8]):
+        with pytest.raises(orc.OracleError):
+            orc.weight_scales(W, 8, "segment", bad)
+
+
+# ------------------------------------------------------------- P7 GEMM ------
+
+def _gemm_ref(c, wc):
+    c = c.astype(np.int64)
+    w = wc.astype(np.int64)
+    return np.maximum(c, 0) @ w.T, np.minimum(c, 0) @ w.T
+
+
+def test_gemm_bruteforce_8x8x8(orc):
+    rng = np.random.default_rng(10)
+    for _ in range(20):
+        c = rng.integers(-128, 128, size=(8, 8)).astype(np.int8)
+        w = rng.integers(-128, 128, size=(8, 8)).astype(np.int8)
+        accp, accn = orc.gemm_dual(c, w)
+        # independent triple loop
+        for i in range(8):
+            for j in range(8):
+                sp = sum(int(c[i, k]) * int(w[j, k]) for k in range(8) if c[i, k] > 0)
+                sn = sum(int(c[i, k]) * int(w[j, k]) for k in range(8) if c[i, k] < 0)
+                assert accp[i, j] == sp and accn[i, j] == sn
+
+
+@pytest.mark.parametrize("M,N,K", [(1, 1, 1), (3, 5, 17), (13, 7, 64), (9, 33, 1040)])
+def test_gemm_random_shapes(orc, M, N, K):
+    rng = np.random.default_rng(M * N + K)
+    c = rng.integers(-127, 128, size=(M, K)).astype(np.int8)
+    w = rng.integers(-127, 128, size=(N, K)).astype(np.int8)
+    accp, accn = orc.gemm_dual(c, w)
+    rp, rn = _gemm_ref(c, w)
+    assert np.array_equal(accp, rp) and np.array_equal(accn, rn)
+    rows = [M - 1, 0]
+    sp, sn = orc.gemm_dual(c, w, rows)
+    assert np.array_equal(sp, rp[rows]) and np.array_equal(sn, rn[rows])
+
+
+def test_gemm_not_transposed(orc):
+    # A non-square case where W^T vs W would differ in shape and value.
+    c = np.array([[1, 2, 3]], np.int8)
+    w = np.array([[1, 0, 0], [0, 0, 1]], np.int8)
+    accp, accn = orc.gemm_dual(c, w)
+    assert accp.tolist() == [[1, 3]] and accn.tolist() == [[0, 0]]
+
+
+def test_gemm_overflow_reported(orc):
+    K = 140000
+    c = np.full((1, K), 127, np.int8)
+    w = np.full((1, K), 127, np.int8)
+    with pytest.raises(orc.OracleError):
+        orc.gemm_dual(c, w)
+
+
+# ---------------------------------------------------------- P8 int4 -------
+
+def test_int4_golden_and_roundtrip(orc):
+    g = _golden("int4_and_lsb.json")
+    for e in g["pack"]:
+        b = orc.pack_int4(np.array([e["codes"]], np.int8))
+        assert b.tolist() == [[e["byte"]]]
+    a, b = np.meshgrid(np.arange(-8, 8), np.arange(-8, 8))
+    codes = np.stack([a.reshape(-1), b.reshape(-1)], axis=1).astype(np.int8).reshape(1, -1)
+    packed = orc.pack_int4(codes)
+    assert np.array_equal(orc.unpack_int4(packed, codes.shape[1]), codes)
+    assert len(set(packed.reshape(-1).tolist())) == 256
+    with pytest.raises(orc.OracleError):
+        orc.pack_int4(np.array([[8, 0]], np.int8))
+
+
+# ----------------------------------------------------------- P9 TASQ -------
+
+def test_lsb_golden(orc):
+    for e in _golden("int4_and_lsb.json")["lsb"]:
+        assert orc.truncate_lsb(e["c"], e["k"]) == e["out"], e
+
+
+def test_lsb_properties_all_codes(orc):
+    for k in range(8):
+        for c in range(-127, 128):
+            t = orc.truncate_lsb(c, k)
+            assert t % (1 << k) == 0
+            assert abs(c - t) < (1 << k) and abs(t) <= abs(c)
+            assert t == 0 or (t > 0) == (c > 0)
+            assert orc.truncate_lsb(t, k) == t
+            # right-shift form of the same operation on the magnitude
+            assert t == int(np.sign(c)) * ((abs(c) >> k) << k)
+            if k == 0:
+                assert t == c
+
+
+def test_quantize_with_lsb(orc):
+    x = synth.silu_normal(11, "t/p9", 20, 64)
+    s = orc.act_scales(x, 8)
+    c0 = orc.quantize_act(x, s, 8, 0).astype(np.int32)
+    for k in (2, 4):
+        ck = orc.quantize_act(x, s, 8, k).astype(np.int32)
+        assert np.array_equal(ck, np.sign(c0) * ((np.abs(c0) >> k) << k))
+    with pytest.raises(orc.OracleError):
+        orc.quantize_act(x, s, 8, 8)
+    with pytest.raises(orc.OracleError):
+        orc.quantize_act(x, s, 4, 4)
+
+
+# ------------------------------------------------------ P10 epilogue/CFG ---
+
+def test_epilogue_unit_scales(orc):
+    rng = np.random.default_rng(12)
+    accp = rng.integers(0, 1 << 20, size=(4, 5)).astype(np.int32)
+    accn = -rng.integers(0, 1 << 20, size=(4, 5)).astype(np.int32)
+    ones = np.ones(2, np.float32)
+    y = orc.epilogue(accp, accn, ones, np.ones(5, np.float32))
+    assert np.array_equal(y, accp.astype(np.float32) + accn.astype(np.float32))
+
+
+def test_epilogue_scales_land_on_their_plane(orc):
+    # acc- must be multiplied by s- and acc+ by s+: swapping them changes y.
+    accp = np.array([[10]], np.int32)
+    accn = np.array([[-3]], np.int32)
+    y = orc.epilogue(accp, accn, np.array([2.0, 5.0], np.float32), np.array([0.5], np.float32))
+    assert y.tolist() == [[(10 * 2 - 3 * 5) * 0.5]]
+    ys = orc.epilogue(accp, accn, np.array([3.0, 3.0], np.float32), np.array([1.0], np.float32),
+                      mode="symmetric")
+    assert ys.tolist() == [[21.0]]
+
+
+def test_epilogue_hadamard_fold_is_power_of_two(orc):
+    rng = np.random.default_rng(13)
+    accp = rng.integers(0, 1 << 24, size=(6, 7)).astype(np.int32)
+    accn = -rng.integers(0, 1 << 24, size=(6, 7)).astype(np.int32)
+    s = np.array([0.013, 0.0021], np.float32)
+    sw = rng.random(7).astype(np.float32)
+    y0 = orc.epilogue(accp, accn, s, sw, 0)
+    for B in (2, 16, 128):
+        yb = orc.epilogue(accp, accn, s, sw, B)
+        assert np.array_equal(yb, y0 / np.float32(B))
+
+
+def test_cfg_properties(orc):
+    rng = np.random.default_rng(14)
+    yc = rng.standard_normal((5, 9)).astype(np.float32)
+    yu = rng.standard_normal((5, 9)).astype(np.float32)
+    assert np.array_equal(orc.cfg_combine(yc, yu, 0.0), yu)
+    out = orc.cfg_combine(yc, yu, 4.0).astype(np.float64)
+    ref = yu.astype(np.float64) + 4.0 * (yc.astype(np.float64) - yu.astype(np.float64))
+    scale = np.abs(yu).astype(np.float64) + 4.0 * np.abs(yc - yu)
+    assert (np.abs(out - ref) <= 3 * 2.0 ** -24 * scale + 1e-30).all()
+    # swapping the branches is not the same combine
+    assert not np.allclose(orc.cfg_combine(yu, yc, 4.0), orc.cfg_combine(yc, yu, 4.0))
+
+
+# ------------------------------------------------------- P11 end to end ----
+
+@pytest.mark.parametrize("a_bits,w_bits,B", [(8, 8, 0), (4, 4, 128), (8, 4, 0), (4, 8, 64)])
+def test_end_to_end_error_bound(orc, a_bits, w_bits, B):
+    M, N, K = 16, 24, 256
+    X = synth.gelu_with_outliers(15, f"t/p11x{a_bits}{w_bits}{B}", M, K)
+    W = synth.weight_normal(15, f"t/p11w{a_bits}{w_bits}{B}", N, K)
+    codes, s = orc.quantize_activations(X, a_bits, B=B)
+    wp = orc.WeightPlan(W, w_bits, B=B)
+    y, _, _ = orc.linear_rows(codes, s, wp, range(M))
+    Xr = (orc.rotate(X, B) if B else X).astype(np.float64)
+    Wr = (orc.rotate(W, B) if B else W).astype(np.float64)
+    exact = Xr @ Wr.T / (B if B else 1)
+    sx = np.where(Xr >= 0, s[0], s[1]).astype(np.float64)  # [M,K]
+    sw = wp.scales.astype(np.float64)  # [N]
+    bound = (np.abs(Xr) @ (np.ones((N, K)) * sw[:, None]).T / 2
+             + sx @ np.abs(Wr).T / 2 + sx @ (np.ones((N, K)) * sw[:, None]).T / 4)
+    bound = bound / (B if B else 1)
+    slack = 1e-5 * (np.abs(Xr) @ np.abs(Wr).T) / (B if B else 1) + 1e-6
+    assert (np.abs(y - exact) <= bound + slack).all()
+
+
+# -------------------------------------------------- P12 tiny exhaustive ----
+
+@pytest.mark.parametrize("a_bits", [4, 8])
+@pytest.mark.parametrize("w_bits", [4, 8])
+@pytest.mark.parametrize("K", [1, 2, 5, 16])
+def test_tiny_dequantized_product(orc, a_bits, w_bits, K):
+    # y must equal the dequantized dot product sum_k (c_k s_pol(k))(wc_k s_w)
+    # up to the few fp32 roundings of the epilogue.
+    X = synth.silu_normal(16, f"t/p12x{K}", 6, K)
+    W = synth.weight_normal(16, f"t/p12w{K}", 5, K)
+    codes, s = orc.quantize_activations(X, a_bits)
+    wp = orc.WeightPlan(W, w_bits)
+    y, accp, accn = orc.linear_rows(codes, s, wp, range(6))
+    c = codes.astype(np.float64)
+    sx = np.where(c > 0, s[0], np.where(c < 0, s[1], 0.0))
+    deq_x = c * sx
+    deq_w = wp.codes.astype(np.float64) * wp.scales[:, None]
+    ref = deq_x @ deq_w.T
+    mag = np.abs(deq_x) @ np.abs(deq_w).T
+    assert (np.abs(y - ref) <= 4 * 2.0 ** -24 * mag + 1e-30).all()
+    qa, qw = orc.qmax(a_bits), orc.qmax(w_bits)
+    assert np.abs(codes).max() <= qa and np.abs(wp.codes).max() <= qw
+
+
+def test_all_int4_code_pairs_in_gemm(orc):
+    # every (activation code, weight code) pair of 4-bit values, one K-slot each
+    a = np.repeat(np.arange(-7, 8), 15).astype(np.int8).reshape(1, -1)
+    w = np.tile(np.arange(-7, 8), 15).astype(np.int8).reshape(1, -1)
+    accp, accn = orc.gemm_dual(a, w)
+    av = np.repeat(np.arange(-7, 8), 15)
+    wv = np.tile(np.arange(-7, 8), 15)
+    assert accp[0, 0] == int((np.maximum(av, 0) * wv).sum())
+    assert accn[0, 0] == int((np.minimum(av, 0) * wv).sum())
+
+
+def test_bf16_conversion_exact(orc):
+    x = synth.normal_f64(17, "t/bf", (1000,)).astype(np.float32)
+    b = synth.f32_to_bf16_bits(x)
+    f = orc.bf16_to_f32(b)
+    assert np.array_equal(f.view(np.uint32) >> 16, b.astype(np.uint32))
+    assert (np.abs(f - x) <= np.abs(x) * 2.0 ** -8).all()
