@@ -1,0 +1,256 @@
+#!/usr/bin/env python3
+"""Benchmark of the quantized linear on one MI355X.
+
+Step = one pass of the hot path over the DiT-XL/2 MLP at W8A8 DualScale with
+the CFG epilogue (16 images x 256 tokens, conditional + unconditional rows,
+M = 4096): for fc1 (1152 -> 4608) and fc2 (4608 -> 1152), quantize the
+activations (dual per-tensor max-reduce + quantize) and run the int8-MFMA GEMM
+with the fused fp32 epilogue and guidance combine (w = 4).
+
+Metric: MFMA int8 TOPS over the step (both DualScale contractions counted,
+4*M*N*K per linear), plus the activation-quantization bandwidth. Inputs are
+seeded synthetic tensors already resident in HBM when timing starts.
+
+Prints ONE JSON line. Other workloads (--workload c1..c5) print their own
+line for reference; the default is the MLP workload.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_INT8_TOPS = 5000.0      # MI355X dense int8 MFMA, 5.0 POP/s
+PEAK_HBM_GBPS = 8000.0       # MI355X HBM3E, 8 TB/s
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=50)
+    p.add_argument("--warmup", type=int, default=10)
+    p.add_argument("--workload", default="mlp", help="mlp (default) | block | c3 | c4")
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--cpu-seconds", type=float, default=12.0,
+                   help="approximate CPU time budget of the oracle baseline")
+    return p.parse_args()
+
+
+def layers_for(name):
+    from workloads import configs
+    if name == "mlp":
+        wl = configs.WORKLOADS["c2"]
+        return wl, [l for l in wl.layers if l.name in ("fc1", "fc2")]
+    if name == "block":
+        wl = configs.WORKLOADS["c2"]
+        return wl, list(wl.layers)
+    if name in ("c3", "c4"):
+        wl = configs.WORKLOADS[name]
+        return wl, list(wl.layers)
+    raise SystemExit(f"unknown workload {name}")
+
+
+class Layer:
+    def __init__(self, torch, wl, L):
+        from bit_post_quantization_amd import QuantLinear
+        from workloads import configs
+        self.L, self.M = L, wl.M
+        X = configs.make_x(wl, L)
+        W = configs.make_w(wl, L)
+        self.X_host, self.W_host = X, W
+        self.X = torch.from_numpy(X.view(np.int16) if L.x_dtype == "bf16" else X).cuda()
+        Wd = torch.from_numpy(W).cuda()
+        seg = L.seg_offsets()
+        self.ql = QuantLinear(Wd, w_bits=L.w_bits, a_bits=L.a_bits, hadamard_block=L.hadamard_block,
+                              seg_offsets=None if seg is None else seg.tolist(),
+                              w_scale=L.w_scale, a_scale=L.a_scale, x_dtype=L.x_dtype)
+        del Wd
+        self.codes = self.ql.alloc_codes(self.M)
+        self.scales = torch.empty(2, dtype=torch.float32, device="cuda")
+        rows = self.M // 2 if L.cfg else self.M
+        self.Y = torch.empty((rows, L.N), dtype=torch.float32, device="cuda")
+        # algorithmic work
+        self.mfma_ops = (2 if L.a_scale == "dual" else 1) * 2.0 * self.M * L.N * L.K
+        self.eff_ops = 2.0 * self.M * L.N * L.K
+        xbytes = 2 if L.x_dtype == "bf16" else 4
+        self.quant_bytes = self.M * L.K * (xbytes + L.a_bits / 8.0)
+
+    def quantize(self):
+        from bit_post_quantization_amd import qlinear_quantize_act
+        qlinear_quantize_act(self.ql.plan, self.X, self.M, 0, None, self.codes, self.scales)
+
+    def gemm(self):
+        from bit_post_quantization_amd import qlinear_gemm
+        qlinear_gemm(self.ql.plan, self.codes, self.scales, self.M, int(self.L.cfg),
+                     self.L.guidance, self.Y)
+
+
+def cpu_baseline(layers, budget_s):
+    """The oracle, as it stands, on a bounded sample of the same workload:
+    every activation code of every layer, and the GEMM + epilogue (+ CFG) on
+    row pairs until the time budget is spent; scaled to the whole step."""
+    import oracle
+    t_quant = 0.0
+    t_gemm_per_row = []
+    rows_done = []
+    per_layer_budget = budget_s / max(1, len(layers))
+    for ly in layers:
+        L = ly.L
+        t0 = time.perf_counter()
+        x = oracle.bf16_to_f32(ly.X_host) if L.x_dtype == "bf16" else ly.X_host
+        codes, s = oracle.quantize_activations(x, L.a_bits, B=L.hadamard_block, mode=L.a_scale)
+        t_quant += time.perf_counter() - t0
+        wp = oracle.WeightPlan(ly.W_host, L.w_bits, B=L.hadamard_block, mode=L.w_scale,
+                               seg_offsets=None if L.seg_offsets() is None else L.seg_offsets())
+        half = ly.M // 2
+        n = 0
+        t0 = time.perf_counter()
+        while True:
+            r = np.array([n, n + half]) if L.cfg else np.array([n])
+            y, _, _ = oracle.linear_rows(codes, s, wp, r, L.a_scale)
+            if L.cfg:
+                oracle.cfg_combine(y[:1], y[1:], L.guidance)
+            n += 1
+            el = time.perf_counter() - t0
+            if (el > per_layer_budget and n >= 2) or n >= (half if L.cfg else ly.M):
+                break
+        rows_done.append(n * (2 if L.cfg else 1))
+        t_gemm_per_row.append(el / (n * (2 if L.cfg else 1)))
+    t_step = t_quant + sum(t * ly.M for t, ly in zip(t_gemm_per_row, layers))
+    ops = sum(ly.mfma_ops for ly in layers)
+    sample = ("full activation quantization of every layer; GEMM+epilogue+CFG on "
+              + ", ".join(f"{r} of {ly.M} rows ({ly.L.name})" for r, ly in zip(rows_done, layers))
+              + "; step time extrapolated linearly in rows")
+    return {"value": ops / t_step / 1e12, "unit": "TOPS", "cores": 1, "kind": "oracle",
+            "sample": sample, "step_seconds_extrapolated": t_step}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1"}))
+        raise SystemExit(2)
+    import torch
+    assert torch.cuda.is_available(), "bench needs a GPU"
+    import bit_post_quantization_amd  # noqa: F401  (raises if libqlinear.so is missing)
+
+    wl, Ls = layers_for(args.workload)
+    layers = [Layer(torch, wl, L) for L in Ls]
+    torch.cuda.synchronize()
+
+    ev = lambda: torch.cuda.Event(enable_timing=True)  # noqa: E731
+    def step(record=None):
+        for i, ly in enumerate(layers):
+            if record is None:
+                ly.quantize()
+                ly.gemm()
+            else:
+                e0, e1, e2 = record[i]
+                e0.record()
+                ly.quantize()
+                e1.record()
+                ly.gemm()
+                e2.record()
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    recs = [[[ev(), ev(), ev()] for _ in layers] for _ in range(args.steps)]
+    start, end = ev(), ev()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    start.record()
+    for k in range(args.steps):
+        step(recs[k])
+    end.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_total = start.elapsed_time(end)
+    ms_step = ms_total / args.steps
+
+    q_ms = np.zeros(len(layers))
+    g_ms = np.zeros(len(layers))
+    for k in range(args.steps):
+        for i in range(len(layers)):
+            e0, e1, e2 = recs[k][i]
+            q_ms[i] += e0.elapsed_time(e1)
+            g_ms[i] += e1.elapsed_time(e2)
+    q_ms /= args.steps
+    g_ms /= args.steps
+
+    step_ops = sum(ly.mfma_ops for ly in layers)
+    value = step_ops / (ms_step * 1e-3) / 1e12
+    # dominant kernel: the GEMM (k2), averaged over its launches in the step
+    gemm_avg_s = float(np.mean(g_ms)) * 1e-3
+    ops_per_launch = float(np.mean([ly.mfma_ops for ly in layers]))
+    gemm_tops = ops_per_launch / gemm_avg_s / 1e12
+    qbytes = sum(ly.quant_bytes for ly in layers)
+    q_gbps = qbytes / (float(np.sum(q_ms)) * 1e-3) / 1e9
+
+    per_layer = []
+    for ly, q, g in zip(layers, q_ms, g_ms):
+        per_layer.append({
+            "layer": ly.L.name, "M": ly.M, "K": ly.L.K, "N": ly.L.N,
+            "quant_us": round(q * 1e3, 2),
+            "quant_gbps": round(ly.quant_bytes / (q * 1e-3) / 1e9, 1),
+            "gemm_us": round(g * 1e3, 2),
+            "gemm_mfma_tops": round(ly.mfma_ops / (g * 1e-3) / 1e12, 1),
+            "gemm_frac_int8_peak": round(ly.mfma_ops / (g * 1e-3) / 1e12 / PEAK_INT8_TOPS, 4),
+        })
+
+    first = wl.layers[0] if args.workload != "mlp" else Ls[0]
+    out = {
+        "metric": "quantized-linear int8 TOPS (% MFMA peak) + act-quant GB/s, DiT-XL/2 MLP",
+        "value": round(value, 2),
+        "unit": "TOPS",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "int8",
+        "data": "synthetic (seeded GELU(N(0,1)) activations with 0.1% x20 outlier channels, N(0,0.02) weights)",
+        "config": {
+            "workload": {"mlp": "DiT-XL/2 MLP fc1 1152->4608 + fc2 4608->1152",
+                         "block": "DiT-XL/2 block QKV+proj+fc1+fc2",
+                         "c3": "DiT-XL/2 block W4A4 + Hadamard-128",
+                         "c4": "MM-DiT SegLinear layers W4 A4/A8"}[args.workload],
+            "M": wl.M, "images": 16, "tokens_per_image": 256, "cfg_guidance": first.guidance,
+            "w_bits": first.w_bits, "a_bits": first.a_bits, "act_scales": first.a_scale,
+            "weight_scales": first.w_scale, "hadamard_block": first.hadamard_block,
+        },
+        "roofline": {
+            "kernel": "k2_gemm (int8 MFMA, both polarity planes, fused epilogue)",
+            "bound": "mfma", "achieved": round(gemm_tops, 1), "peak": PEAK_INT8_TOPS,
+            "unit": "TOPS", "frac": round(gemm_tops / PEAK_INT8_TOPS, 4),
+            "ops_per_launch": ops_per_launch, "avg_launch_us": round(gemm_avg_s * 1e6, 2),
+            "traffic": None,
+        },
+        "act_quant": {
+            "kernels": "k1_reduce + k1_quantize", "bound": "hbm",
+            "achieved": round(q_gbps, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
+            "frac": round(q_gbps / PEAK_HBM_GBPS, 4),
+            "bytes_per_step": qbytes,
+        },
+        "effective_tops": round(sum(ly.eff_ops for ly in layers) / (ms_step * 1e-3) / 1e12, 2),
+        "layers": per_layer,
+        "wall_s": round(wall, 3),
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(layers, args.cpu_seconds)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,195 @@
+// K0 (offline plan kernels) and K3 (standalone CFG combine).
+//
+// K0 follows the weight side of the method: optional block Walsh-Hadamard
+// rotation of the weight rows (HQ-DM explainer 2.1 applied to both operands),
+// symmetric absmax scales per output channel or per output segment
+// (SegQuant explainer 2.A: each chunk of a segmented linear's output is
+// quantized on its own), round-half-even codes, 4-bit packing.
+// K3 is the guided prediction of the "Closing the Null Space" explainer,
+// problem statement.
+#include "ql_device.h"
+#include "ql_kernels.h"
+
+namespace ql {
+
+namespace {
+
+// In-place rotation of W [N,K] as a flat stream of 4-float units.
+template <int HB>
+__global__ __launch_bounds__(256) void k0_rotate(float* W, int64_t nunits) {
+  const int lane = threadIdx.x & 63;
+  const int64_t base = ((int64_t)blockIdx.x * 4 + (threadIdx.x >> 6)) * 64;
+  const int64_t idx = base + lane;
+  float e[4] = {0.f, 0.f, 0.f, 0.f};
+  float4* p = reinterpret_cast<float4*>(W);
+  if (idx < nunits) {
+    const float4 v = p[idx];
+    e[0] = v.x;
+    e[1] = v.y;
+    e[2] = v.z;
+    e[3] = v.w;
+  }
+  fwht_block<HB>(e, lane);
+  if (idx < nunits) p[idx] = make_float4(e[0], e[1], e[2], e[3]);
+}
+
+// Bits of max_k |W[n,k]| per row (one block per row).
+__global__ __launch_bounds__(256) void k0_row_absmax(const float* W, int K, uint32_t* rowmax) {
+  const int64_t n = blockIdx.x;
+  const float* row = W + n * K;
+  uint32_t m = 0;
+  for (int k = threadIdx.x; k < K; k += 256) {
+    const uint32_t b = __float_as_uint(row[k]) & 0x7FFFFFFFu;
+    m = b > m ? b : m;
+  }
+  m = wave_max_u32(m);
+  __shared__ uint32_t sm[4];
+  if ((threadIdx.x & 63) == 0) sm[threadIdx.x >> 6] = m;
+  __syncthreads();
+  if (threadIdx.x == 0) rowmax[n] = max(max(sm[0], sm[1]), max(sm[2], sm[3]));
+}
+
+// Per channel: s[n] = rowmax[n] / qw. Per segment: one block per segment,
+// s = (max over its rows) / qw written to every row of the segment.
+__global__ __launch_bounds__(256) void k0_scales_channel(const uint32_t* rowmax, int N, float qw,
+                                                         float* sw) {
+  const int n = blockIdx.x * 256 + threadIdx.x;
+  if (n < N) sw[n] = __uint_as_float(rowmax[n]) / qw;
+}
+
+__global__ __launch_bounds__(256) void k0_scales_segment(const uint32_t* rowmax, const int32_t* seg,
+                                                         float qw, float* sw) {
+  const int lo = seg[blockIdx.x], hi = seg[blockIdx.x + 1];
+  uint32_t m = 0;
+  for (int n = lo + threadIdx.x; n < hi; n += 256) m = rowmax[n] > m ? rowmax[n] : m;
+  m = wave_max_u32(m);
+  __shared__ uint32_t sm[4];
+  __shared__ float s;
+  if ((threadIdx.x & 63) == 0) sm[threadIdx.x >> 6] = m;
+  __syncthreads();
+  if (threadIdx.x == 0) s = __uint_as_float(max(max(sm[0], sm[1]), max(sm[2], sm[3]))) / qw;
+  __syncthreads();
+  for (int n = lo + threadIdx.x; n < hi; n += 256) sw[n] = s;
+}
+
+__device__ __forceinline__ int quant_sym(float v, float s, float q) {
+  float r = rintf(v / s);
+  r = fminf(fmaxf(r, -q), q);
+  return s > 0.0f ? (int)r : 0;
+}
+
+// Codes of 4 consecutive weights of one row per thread (K % 4 == 0).
+template <bool W4>
+__global__ __launch_bounds__(256) void k0_quant_w(const float* W, const float* sw, int K,
+                                                  int64_t nunits, float qw, uint8_t* out) {
+  const int64_t u = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (u >= nunits) return;
+  const int64_t n = (u * 4) / K;
+  const float s = sw[n];
+  const float4 v = reinterpret_cast<const float4*>(W)[u];
+  const int c0 = quant_sym(v.x, s, qw), c1 = quant_sym(v.y, s, qw);
+  const int c2 = quant_sym(v.z, s, qw), c3 = quant_sym(v.w, s, qw);
+  if constexpr (W4) {
+    reinterpret_cast<uint16_t*>(out)[u] =
+        (uint16_t)((c0 & 0xF) | ((c1 & 0xF) << 4) | ((c2 & 0xF) << 8) | ((c3 & 0xF) << 12));
+  } else {
+    reinterpret_cast<uint32_t*>(out)[u] =
+        (uint32_t)(c0 & 0xFF) | ((uint32_t)(c1 & 0xFF) << 8) | ((uint32_t)(c2 & 0xFF) << 16) |
+        ((uint32_t)(c3 & 0xFF) << 24);
+  }
+}
+
+// Plan codes -> int8 [N,K] (sign-extended nibbles for 4-bit plans).
+template <bool W4>
+__global__ __launch_bounds__(256) void k0_unpack(const uint8_t* in, int64_t n_elems, int8_t* out) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= n_elems) return;
+  if constexpr (W4) {
+    const int b = in[i >> 1];
+    int v = (i & 1) ? (b >> 4) & 0xF : b & 0xF;
+    out[i] = (int8_t)(v >= 8 ? v - 16 : v);
+  } else {
+    out[i] = (int8_t)in[i];
+  }
+}
+
+// K3: out = yu + w * (yc - yu); yc = Y[e], yu = Y[e + half].
+__global__ __launch_bounds__(256) void k3_cfg(const float* Y, int64_t half, float w, float* out) {
+  const int64_t stride = (int64_t)gridDim.x * 256;
+  for (int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x; e < half; e += stride) {
+    const float yc = Y[e];
+    const float yu = Y[e + half];
+    const float d = __fsub_rn(yc, yu);
+    const float t = __fmul_rn(w, d);
+    out[e] = __fadd_rn(yu, t);
+  }
+}
+
+int blocks_for(int64_t n, int64_t per) {
+  int64_t b = (n + per - 1) / per;
+  return (int)(b < 1 ? 1 : b);
+}
+
+}  // namespace
+
+hipError_t launch_rotate_rows(float* W, int64_t nunits, int hb, hipStream_t s) {
+  const dim3 grid(blocks_for(nunits, 256));
+  switch (hb) {
+    case 4: hipLaunchKernelGGL((k0_rotate<4>), grid, dim3(256), 0, s, W, nunits); break;
+    case 8: hipLaunchKernelGGL((k0_rotate<8>), grid, dim3(256), 0, s, W, nunits); break;
+    case 16: hipLaunchKernelGGL((k0_rotate<16>), grid, dim3(256), 0, s, W, nunits); break;
+    case 32: hipLaunchKernelGGL((k0_rotate<32>), grid, dim3(256), 0, s, W, nunits); break;
+    case 64: hipLaunchKernelGGL((k0_rotate<64>), grid, dim3(256), 0, s, W, nunits); break;
+    case 128: hipLaunchKernelGGL((k0_rotate<128>), grid, dim3(256), 0, s, W, nunits); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_row_absmax(const float* W, int N, int K, uint32_t* rowmax, hipStream_t s) {
+  hipLaunchKernelGGL(k0_row_absmax, dim3(N), dim3(256), 0, s, W, K, rowmax);
+  return hipGetLastError();
+}
+
+hipError_t launch_weight_scales(const uint32_t* rowmax, int N, int mode, const int32_t* seg,
+                                int nseg, float qw, float* sw, hipStream_t s) {
+  if (mode == 2) {
+    hipLaunchKernelGGL(k0_scales_channel, dim3(blocks_for(N, 256)), dim3(256), 0, s, rowmax, N,
+                       qw, sw);
+  } else {
+    hipLaunchKernelGGL(k0_scales_segment, dim3(nseg), dim3(256), 0, s, rowmax, seg, qw, sw);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_quantize_weights(const float* W, const float* sw, int N, int K, int w4, float qw,
+                                   uint8_t* out, hipStream_t s) {
+  const int64_t nunits = (int64_t)N * K / 4;
+  const dim3 grid(blocks_for(nunits, 256));
+  if (w4)
+    hipLaunchKernelGGL((k0_quant_w<true>), grid, dim3(256), 0, s, W, sw, K, nunits, qw, out);
+  else
+    hipLaunchKernelGGL((k0_quant_w<false>), grid, dim3(256), 0, s, W, sw, K, nunits, qw, out);
+  return hipGetLastError();
+}
+
+hipError_t launch_unpack_weights(const uint8_t* in, int N, int K, int w4, int8_t* out,
+                                 hipStream_t s) {
+  const int64_t n = (int64_t)N * K;
+  const dim3 grid(blocks_for(n, 256));
+  if (w4)
+    hipLaunchKernelGGL((k0_unpack<true>), grid, dim3(256), 0, s, in, n, out);
+  else
+    hipLaunchKernelGGL((k0_unpack<false>), grid, dim3(256), 0, s, in, n, out);
+  return hipGetLastError();
+}
+
+hipError_t launch_cfg_combine(const float* Y, int64_t half, float w, float* out, hipStream_t s) {
+  int64_t b = (half + 255) / 256;
+  if (b > 8192) b = 8192;
+  if (b < 1) b = 1;
+  hipLaunchKernelGGL(k3_cfg, dim3((int)b), dim3(256), 0, s, Y, half, w, out);
+  return hipGetLastError();
+}
+
+}  // namespace ql

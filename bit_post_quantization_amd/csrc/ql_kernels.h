@@ -1,0 +1,65 @@
+// Internal interface between the C ABI (qlinear_api.cpp) and the kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace ql {
+
+// Reduction workspace of one plan: per-block partial maxima written by the
+// max-reduce kernel and read by the quantize kernel of the same call (stream
+// order makes them visible; nothing needs clearing between calls).
+constexpr int kMaxReduceBlocks = 1024;
+struct ReduceWs {
+  uint32_t part[2][kMaxReduceBlocks];  // bits of max(+0, max x), max(+0, -min x)
+};
+
+struct QuantArgs {
+  const void* X;
+  int64_t nunits;            // number of 4-element units (M*K/4)
+  void* codes;
+  float* act_scales;         // out [2]
+  const float* static_scales;// in [2] or nullptr
+  ReduceWs* ws;
+  int reduce_blocks;         // partials written by the reduce kernel
+  float qa;
+  int keep_mask;             // ~((1 << lsb_k) - 1)
+  int sym;
+};
+
+struct GemmArgs {
+  const uint8_t* A;          // activation codes: int8 [M,K] or packed [M,K/2]
+  const uint8_t* W;          // weight codes: int8 [N,K] or packed [N,K/2]
+  const float* act_scales;   // [2]
+  const float* w_scales;     // [N]
+  float* Y;                  // [M,N] or [M/2,N]
+  int32_t* dbg;              // [2,M,N] or nullptr
+  int M, N, K;
+  int Mh;                    // M/2 with CFG pairing
+  int64_t lda, ldw;          // bytes per row of A / W
+  float guidance;
+  float inv_b;               // 1/B (rotation) or 1
+};
+
+// K1: activation quantization. Returns the launch status.
+hipError_t launch_quantize(const QuantArgs& a, int x_bf16, int hadamard_block, int a4,
+                           hipStream_t s);
+
+// K2: GEMM + epilogue.
+hipError_t launch_gemm(const GemmArgs& g, int a4, int w4, int sym, int cfg, hipStream_t s);
+
+// K3: standalone CFG combine.
+hipError_t launch_cfg_combine(const float* Y, int64_t half_elems, float w, float* out,
+                              hipStream_t s);
+
+// K0: plan kernels.
+hipError_t launch_rotate_rows(float* W, int64_t nunits, int hadamard_block, hipStream_t s);
+hipError_t launch_row_absmax(const float* W, int N, int K, uint32_t* rowmax, hipStream_t s);
+hipError_t launch_weight_scales(const uint32_t* rowmax, int N, int mode, const int32_t* seg,
+                                int nseg, float qw, float* sw, hipStream_t s);
+hipError_t launch_quantize_weights(const float* W, const float* sw, int N, int K, int w4,
+                                   float qw, uint8_t* out, hipStream_t s);
+hipError_t launch_unpack_weights(const uint8_t* in, int N, int K, int w4, int8_t* out,
+                                 hipStream_t s);
+
+}  // namespace ql

@@ -1,0 +1,297 @@
+// C ABI of libqlinear.so (declared in include/qlinear.h): argument checks,
+// the plan object, and the launches of the HIP kernels on the caller's
+// stream. No computation of the method happens here.
+#include "../../include/qlinear.h"
+
+#include <hip/hip_runtime.h>
+
+#include <cstdarg>
+#include <cstdio>
+#include <string>
+#include <vector>
+
+#include "ql_kernels.h"
+
+struct qlinear_plan {
+  ql_desc d;
+  std::vector<int32_t> seg;  // host copy, n_segments + 1
+  int device = -1;
+  uint8_t* wq = nullptr;     // weight codes, int8 [N,K] or packed [N,K/2]
+  float* sw = nullptr;       // weight scales [N]
+  ql::ReduceWs* ws = nullptr;
+};
+
+namespace {
+
+thread_local std::string g_err;
+
+ql_status fail(ql_status st, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return st;
+}
+
+ql_status ok() {
+  g_err.clear();
+  return QL_OK;
+}
+
+ql_status hip_fail(hipError_t e, const char* what) {
+  return fail(e == hipErrorOutOfMemory ? QL_ERR_OOM : QL_ERR_HIP, "%s: %s", what,
+              hipGetErrorString(e));
+}
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+int qmax(int bits) { return (1 << (bits - 1)) - 1; }
+
+ql_status check_desc(const ql_desc* d) {
+  if (!d) return fail(QL_ERR_ARG, "descriptor is NULL");
+  if (d->N < 1) return fail(QL_ERR_ARG, "N = %d must be >= 1", d->N);
+  if (d->K < 16 || d->K > 65536) return fail(QL_ERR_ARG, "K = %d must be in [16, 65536]", d->K);
+  if ((d->w_bits != 4 && d->w_bits != 8) || (d->a_bits != 4 && d->a_bits != 8))
+    return fail(QL_ERR_ARG, "w_bits = %d and a_bits = %d must each be 4 or 8", d->w_bits, d->a_bits);
+  const bool any4 = d->w_bits == 4 || d->a_bits == 4;
+  if (any4 && d->K % 32 != 0)
+    return fail(QL_ERR_ARG, "K = %d must be a multiple of 32 with 4-bit codes", d->K);
+  if (d->K % 16 != 0) return fail(QL_ERR_ARG, "K = %d must be a multiple of 16", d->K);
+  const int hb = d->hadamard_block;
+  if (hb != 0) {
+    if (hb < 0 || (hb & (hb - 1)) != 0)
+      return fail(QL_ERR_ARG, "hadamard_block = %d must be 0 or a power of two", hb);
+    if (d->K % hb != 0)
+      return fail(QL_ERR_ARG, "K = %d is not a multiple of hadamard_block = %d", d->K, hb);
+    if (hb < 4 || hb > 128)
+      return fail(QL_ERR_UNSUPPORTED, "hadamard_block = %d: supported blocks are 4..128", hb);
+  }
+  if (d->w_scale_mode != QL_WSCALE_PER_TENSOR && d->w_scale_mode != QL_WSCALE_PER_SEGMENT &&
+      d->w_scale_mode != QL_WSCALE_PER_CHANNEL)
+    return fail(QL_ERR_ARG, "bad w_scale_mode %d", (int)d->w_scale_mode);
+  if (d->a_scale_mode != QL_ASCALE_DUAL && d->a_scale_mode != QL_ASCALE_SYMMETRIC)
+    return fail(QL_ERR_ARG, "bad a_scale_mode %d", (int)d->a_scale_mode);
+  if (d->x_dtype != QL_F32 && d->x_dtype != QL_BF16)
+    return fail(QL_ERR_ARG, "bad x_dtype %d", (int)d->x_dtype);
+  if (d->n_segments < 1) return fail(QL_ERR_ARG, "n_segments = %d must be >= 1", d->n_segments);
+  if (d->n_segments > 1 && !d->seg_offsets)
+    return fail(QL_ERR_ARG, "seg_offsets is NULL with n_segments = %d", d->n_segments);
+  if (d->seg_offsets) {
+    const int32_t* o = d->seg_offsets;
+    if (o[0] != 0 || o[d->n_segments] != d->N)
+      return fail(QL_ERR_ARG, "segments must start at 0 and end at N = %d", d->N);
+    for (int g = 0; g < d->n_segments; ++g)
+      if (o[g + 1] <= o[g]) return fail(QL_ERR_ARG, "segment %d is empty or descending", g);
+  }
+  return QL_OK;
+}
+
+ql_status check_plan(qlinear_plan_t p) {
+  if (!p) return fail(QL_ERR_ARG, "plan is NULL");
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess) return fail(QL_ERR_HIP, "hipGetDevice failed");
+  if (dev != p->device)
+    return fail(QL_ERR_ARG, "current device %d is not the plan's device %d", dev, p->device);
+  return QL_OK;
+}
+
+void free_plan(struct qlinear_plan* p) {
+  if (!p) return;
+  if (p->wq) (void)hipFree(p->wq);
+  if (p->sw) (void)hipFree(p->sw);
+  if (p->ws) (void)hipFree(p->ws);
+  delete p;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* qlinear_last_error(void) { return g_err.c_str(); }
+
+const char* qlinear_version(void) { return "qlinear 0.1.0 gfx950"; }
+
+ql_status qlinear_plan(const ql_desc* d, const float* W, void* stream, qlinear_plan_t* out) {
+  ql_status st = check_desc(d);
+  if (st != QL_OK) return st;
+  if (!W || !out) return fail(QL_ERR_ARG, "W or out is NULL");
+  if (!aligned(W, 16)) return fail(QL_ERR_ARG, "W must be 16-byte aligned");
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  auto* p = new struct qlinear_plan();
+  p->d = *d;
+  if (d->seg_offsets) {
+    p->seg.assign(d->seg_offsets, d->seg_offsets + d->n_segments + 1);
+  } else {
+    p->seg = {0, d->N};
+    p->d.n_segments = 1;
+  }
+  p->d.seg_offsets = nullptr;
+  if (hipGetDevice(&p->device) != hipSuccess) {
+    free_plan(p);
+    return fail(QL_ERR_HIP, "hipGetDevice failed");
+  }
+  const int64_t N = d->N, K = d->K;
+  const size_t wbytes = (size_t)(d->w_bits == 4 ? N * K / 2 : N * K);
+  float* rot = nullptr;
+  uint32_t* rowmax = nullptr;
+  int32_t* segd = nullptr;
+  hipError_t e = hipSuccess;
+  auto cleanup = [&]() {
+    if (rot) (void)hipFree(rot);
+    if (rowmax) (void)hipFree(rowmax);
+    if (segd) (void)hipFree(segd);
+  };
+#define QL_TRY(expr, what)          \
+  do {                              \
+    e = (expr);                     \
+    if (e != hipSuccess) {          \
+      cleanup();                    \
+      free_plan(p);                 \
+      return hip_fail(e, what);     \
+    }                               \
+  } while (0)
+  QL_TRY(hipMalloc(&p->wq, wbytes), "allocating weight codes");
+  QL_TRY(hipMalloc(&p->sw, N * sizeof(float)), "allocating weight scales");
+  QL_TRY(hipMalloc(&p->ws, sizeof(ql::ReduceWs)), "allocating reduction workspace");
+  QL_TRY(hipMalloc(&rowmax, N * sizeof(uint32_t)), "allocating row maxima");
+  // Offsets that define the scale groups: the given segments for
+  // PER_SEGMENT, one group [0,N) for PER_TENSOR (unused for PER_CHANNEL).
+  const int mode = d->w_scale_mode == QL_WSCALE_PER_SEGMENT  ? 1
+                   : d->w_scale_mode == QL_WSCALE_PER_TENSOR ? 0
+                                                             : 2;
+  const std::vector<int32_t> groups =
+      mode == 1 ? p->seg : std::vector<int32_t>{0, (int32_t)N};
+  const int ngroups = (int)groups.size() - 1;
+  QL_TRY(hipMalloc(&segd, groups.size() * sizeof(int32_t)), "allocating segment offsets");
+  QL_TRY(hipMemcpyAsync(segd, groups.data(), groups.size() * sizeof(int32_t),
+                        hipMemcpyHostToDevice, s),
+         "copying segment offsets");
+  const float* src = W;
+  if (d->hadamard_block) {
+    QL_TRY(hipMalloc(&rot, N * K * sizeof(float)), "allocating rotation buffer");
+    QL_TRY(hipMemcpyAsync(rot, W, N * K * sizeof(float), hipMemcpyDeviceToDevice, s),
+           "copying W");
+    QL_TRY(ql::launch_rotate_rows(rot, N * K / 4, d->hadamard_block, s), "rotating W");
+    src = rot;
+  }
+  const float qw = (float)qmax(d->w_bits);
+  QL_TRY(ql::launch_row_absmax(src, (int)N, (int)K, rowmax, s), "weight row maxima");
+  QL_TRY(ql::launch_weight_scales(rowmax, (int)N, mode, segd, ngroups, qw, p->sw, s),
+         "weight scales");
+  QL_TRY(ql::launch_quantize_weights(src, p->sw, (int)N, (int)K, d->w_bits == 4, qw, p->wq, s),
+         "weight codes");
+  QL_TRY(hipStreamSynchronize(s), "synchronising plan stream");
+#undef QL_TRY
+  cleanup();
+  *out = p;
+  return ok();
+}
+
+ql_status qlinear_plan_destroy(qlinear_plan_t p) {
+  free_plan(p);
+  return ok();
+}
+
+ql_status qlinear_plan_weights(qlinear_plan_t p, int8_t* w_codes, float* w_scales, void* stream) {
+  ql_status st = check_plan(p);
+  if (st != QL_OK) return st;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  hipError_t e;
+  if (w_codes) {
+    e = ql::launch_unpack_weights(p->wq, p->d.N, p->d.K, p->d.w_bits == 4, w_codes, s);
+    if (e != hipSuccess) return hip_fail(e, "unpacking weight codes");
+  }
+  if (w_scales) {
+    e = hipMemcpyAsync(w_scales, p->sw, (size_t)p->d.N * sizeof(float), hipMemcpyDeviceToDevice, s);
+    if (e != hipSuccess) return hip_fail(e, "copying weight scales");
+  }
+  return ok();
+}
+
+ql_status qlinear_quantize_act(qlinear_plan_t p, const void* X, int32_t M, int32_t lsb_k,
+                               const float* static_scales, void* codes, float* act_scales,
+                               void* stream) {
+  ql_status st = check_plan(p);
+  if (st != QL_OK) return st;
+  if (M < 0) return fail(QL_ERR_ARG, "M = %d must be >= 0", M);
+  if (lsb_k < 0 || lsb_k >= p->d.a_bits)
+    return fail(QL_ERR_ARG, "lsb_k = %d must be in [0, %d)", lsb_k, p->d.a_bits);
+  if (M == 0) return ok();  // empty tensors may carry NULL data pointers
+  if (!X || !codes || !act_scales) return fail(QL_ERR_ARG, "X, codes or act_scales is NULL");
+  const bool bf16 = p->d.x_dtype == QL_BF16;
+  if (!aligned(X, bf16 ? 8 : 16)) return fail(QL_ERR_ARG, "X is not %d-byte aligned", bf16 ? 8 : 16);
+  if (!aligned(codes, 16)) return fail(QL_ERR_ARG, "codes must be 16-byte aligned");
+  if (!aligned(act_scales, 4) || (static_scales && !aligned(static_scales, 4)))
+    return fail(QL_ERR_ARG, "scale pointers must be 4-byte aligned");
+  ql::QuantArgs a;
+  a.X = X;
+  a.nunits = (int64_t)M * p->d.K / 4;
+  a.codes = codes;
+  a.act_scales = act_scales;
+  a.static_scales = static_scales;
+  a.ws = p->ws;
+  a.reduce_blocks = 0;
+  a.qa = (float)qmax(p->d.a_bits);
+  a.keep_mask = ~((1 << lsb_k) - 1);
+  a.sym = p->d.a_scale_mode == QL_ASCALE_SYMMETRIC;
+  hipError_t e = ql::launch_quantize(a, bf16, p->d.hadamard_block, p->d.a_bits == 4,
+                                     reinterpret_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "launching quantize");
+  return ok();
+}
+
+ql_status qlinear_gemm(qlinear_plan_t p, const void* codes, const float* act_scales, int32_t M,
+                       int32_t cfg, float w, float* Y, int32_t* acc_dbg, void* stream) {
+  ql_status st = check_plan(p);
+  if (st != QL_OK) return st;
+  if (M < 0) return fail(QL_ERR_ARG, "M = %d must be >= 0", M);
+  if (M > (1 << 23)) return fail(QL_ERR_UNSUPPORTED, "M = %d exceeds 8388608 rows", M);
+  if (cfg != 0 && cfg != 1) return fail(QL_ERR_ARG, "cfg = %d must be 0 or 1", cfg);
+  if (cfg && (M % 2)) return fail(QL_ERR_ARG, "M = %d must be even with cfg = 1", M);
+  if (M == 0) return ok();  // empty tensors may carry NULL data pointers
+  if (!codes || !act_scales || !Y) return fail(QL_ERR_ARG, "codes, act_scales or Y is NULL");
+  if (!aligned(codes, 16)) return fail(QL_ERR_ARG, "codes must be 16-byte aligned");
+  if (!aligned(Y, 4) || !aligned(act_scales, 4) || (acc_dbg && !aligned(acc_dbg, 4)))
+    return fail(QL_ERR_ARG, "Y, act_scales and acc_dbg must be 4-byte aligned");
+  ql::GemmArgs g;
+  g.A = reinterpret_cast<const uint8_t*>(codes);
+  g.W = p->wq;
+  g.act_scales = act_scales;
+  g.w_scales = p->sw;
+  g.Y = Y;
+  g.dbg = acc_dbg;
+  g.M = M;
+  g.N = p->d.N;
+  g.K = p->d.K;
+  g.Mh = cfg ? M / 2 : M;
+  g.lda = p->d.a_bits == 4 ? p->d.K / 2 : p->d.K;
+  g.ldw = p->d.w_bits == 4 ? p->d.K / 2 : p->d.K;
+  g.guidance = w;
+  g.inv_b = p->d.hadamard_block ? 1.0f / (float)p->d.hadamard_block : 1.0f;
+  hipError_t e = ql::launch_gemm(g, p->d.a_bits == 4, p->d.w_bits == 4,
+                                 p->d.a_scale_mode == QL_ASCALE_SYMMETRIC, cfg,
+                                 reinterpret_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "launching gemm");
+  return ok();
+}
+
+ql_status qlinear_cfg_combine(const float* Y, int32_t M, int32_t N, float w, float* out,
+                              void* stream) {
+  if (M < 0 || N < 1) return fail(QL_ERR_ARG, "M = %d, N = %d: need M >= 0, N >= 1", M, N);
+  if (M % 2) return fail(QL_ERR_ARG, "M = %d must be even", M);
+  if (M == 0) return ok();
+  if (!Y || !out) return fail(QL_ERR_ARG, "Y or out is NULL");
+  if (!aligned(Y, 4) || !aligned(out, 4)) return fail(QL_ERR_ARG, "Y and out must be 4-byte aligned");
+  const int64_t half = (int64_t)(M / 2) * N;
+  const uintptr_t y0 = reinterpret_cast<uintptr_t>(Y), y1 = y0 + 2 * half * sizeof(float);
+  const uintptr_t o0 = reinterpret_cast<uintptr_t>(out), o1 = o0 + half * sizeof(float);
+  if (half > 0 && o0 < y1 && y0 < o1) return fail(QL_ERR_ARG, "out overlaps Y");
+  if (half == 0) return ok();
+  hipError_t e = ql::launch_cfg_combine(Y, half, w, out, reinterpret_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "launching cfg_combine");
+  return ok();
+}
+
+}  // extern "C"

@@ -1,0 +1,183 @@
+/*
+ * qlinear.h -- C ABI of libqlinear.so: the quantized linear layer of a
+ * diffusion transformer on AMD Instinct MI355X (gfx950).
+ *
+ *   Y = dequant( Q_w(W') * Q_a(X') )        X' = X H, W' = W H (optional)
+ *
+ * computed in four steps, each in hand-written HIP kernels:
+ *   1. optional block Walsh-Hadamard rotation of X (and of W at plan time)
+ *      -- HQ-DM explainer, technical summary 2.1 (block-diagonal H built
+ *      from standard Hadamard matrices; the normalisation is a power of two
+ *      folded into the float scales so the core stays integer);
+ *   2. DualScale activation quantization: one scale for the non-negative
+ *      region and one for the negative region, codes int8 or int4, optional
+ *      truncation of k low bits of every code -- SegQuant explainer,
+ *      technical summary 2.B; TASQ explainer, technical summary 2;
+ *   3. integer GEMM of both polarity planes against the weight codes, with
+ *      weight scales per output channel, per output segment or per tensor --
+ *      SegQuant explainer 2.A (output segmentation) and 2.B (two products
+ *      run as one batched GEMM);
+ *   4. fp32 epilogue: scaled sum of the two products, optionally fused with
+ *      the classifier-free-guidance combine uncond + w * (cond - uncond) --
+ *      "Closing the Null Space" explainer, problem statement.
+ *
+ * Conventions for every call:
+ *   - Tensor pointers are DEVICE pointers on the device that was current
+ *     when the plan was made, row-major and contiguous, owned by the caller;
+ *     the library never frees or retains them. Host pointers are marked HOST.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the null stream).
+ *     All work is enqueued asynchronously on it; no call synchronises the
+ *     host or copies device data to the host, except qlinear_plan (below).
+ *   - Arguments are validated on the host before anything is enqueued; a
+ *     violation returns QL_ERR_ARG (or QL_ERR_UNSUPPORTED for a valid but
+ *     unimplemented combination) and enqueues nothing. A failed HIP launch
+ *     or allocation returns QL_ERR_HIP / QL_ERR_OOM. qlinear_last_error()
+ *     then gives a message (thread-local; valid until the next call on that
+ *     thread).
+ *   - Inputs must be finite; non-finite values give unspecified codes.
+ *   - A plan is immutable after qlinear_plan returns, except for a small
+ *     internal reduction workspace used by qlinear_quantize_act: calls of
+ *     qlinear_quantize_act with dynamic scales on one plan must be ordered
+ *     (one stream, or explicit events); other calls may run concurrently.
+ */
+#ifndef QLINEAR_H
+#define QLINEAR_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct qlinear_plan* qlinear_plan_t; /* opaque, owned by the library */
+
+typedef enum {
+  QL_OK = 0,
+  QL_ERR_ARG = 1,
+  QL_ERR_UNSUPPORTED = 2,
+  QL_ERR_OOM = 3,
+  QL_ERR_HIP = 4
+} ql_status;
+
+typedef enum { QL_F32 = 0, QL_BF16 = 1 } ql_dtype;
+
+/* Weight-scale granularity (SegQuant explainer 2.A: each output segment of a
+ * chunked linear is quantized on its own). PER_TENSOR is one segment. */
+typedef enum {
+  QL_WSCALE_PER_TENSOR = 0,
+  QL_WSCALE_PER_SEGMENT = 1,
+  QL_WSCALE_PER_CHANNEL = 2
+} ql_wscale;
+
+/* Activation scales: DUAL = separate s+ / s- for the non-negative and the
+ * negative region (SegQuant explainer 2.B); SYMMETRIC = one scale
+ * max|x|/qmax for both (HQ-DM explainer 2.2 uses symmetric activations). */
+typedef enum { QL_ASCALE_DUAL = 0, QL_ASCALE_SYMMETRIC = 1 } ql_ascale;
+
+typedef struct {
+  int32_t N, K;              /* W is [N,K]; Y = X W^T. 1 <= N, 16 <= K <= 65536 */
+  int32_t w_bits, a_bits;    /* each 8 or 4 */
+  int32_t hadamard_block;    /* 0 = no rotation; else B in {4,8,...,128}, K % B == 0 */
+  int32_t n_segments;        /* >= 1 output segments partitioning [0,N) */
+  const int32_t* seg_offsets;/* HOST [n_segments+1]: 0 = o_0 < o_1 < ... < o_n = N;
+                                NULL means one segment [0,N) */
+  ql_wscale w_scale_mode;
+  ql_ascale a_scale_mode;
+  ql_dtype x_dtype;          /* dtype of X given to qlinear_quantize_act */
+} ql_desc;
+
+/* Shape rules checked by every call: K % 16 == 0 when both w_bits and
+ * a_bits are 8, K % 32 == 0 when either is 4. */
+
+/*
+ * Build a plan for one linear layer: rotate the rows of W block-wise by the
+ * unnormalised Sylvester Hadamard matrix of order hadamard_block (stages of
+ * butterfly distance 1, 2, ..., B/2, each (a,b) -> (a+b, a-b) in fp32), take
+ * the symmetric absmax weight scale per channel / segment / tensor
+ * (s = absmax / qmax_w, qmax_w = 2^(w_bits-1) - 1), quantize
+ * (round half to even, clamp to [-qmax_w, qmax_w]) and pack 4-bit codes two
+ * per byte (element 2j in bits 0-3 and 2j+1 in bits 4-7 of byte j).
+ *   d   : HOST descriptor (copied; seg_offsets copied too).
+ *   W   : DEVICE fp32 [N,K]; read only, may be freed after the call.
+ *   out : HOST; receives the plan handle.
+ * Allocates device memory for the plan and synchronises `stream` before it
+ * returns (plan building is offline work). Errors: QL_ERR_ARG for a bad
+ * descriptor or NULL pointer, QL_ERR_OOM, QL_ERR_HIP.
+ */
+ql_status qlinear_plan(const ql_desc* d, const float* W, void* stream, qlinear_plan_t* out);
+
+/* Free a plan's device memory. The caller ensures no enqueued work still
+ * uses it (synchronise first). NULL is accepted. */
+ql_status qlinear_plan_destroy(qlinear_plan_t p);
+
+/* Copy a plan's weights out for inspection: w_codes DEVICE int8 [N,K]
+ * (unpacked, one code per byte), w_scales DEVICE fp32 [N]. Either may be
+ * NULL to skip it. */
+ql_status qlinear_plan_weights(qlinear_plan_t p, int8_t* w_codes, float* w_scales, void* stream);
+
+/*
+ * Quantize activations X [M,K] (x_dtype of the plan) to codes.
+ * Steps per element: optional block rotation (as for W), then per-tensor
+ * scales over all M*K rotated values: s+ = max(0, max x)/qa and
+ * s- = max(0, -min x)/qa with qa = 2^(a_bits-1) - 1 (SYMMETRIC: both equal
+ * max(0, max x, -min x)/qa), or the given static scales; then
+ * x >= 0 -> round_half_even(x / s+) clamped to [0, qa], x < 0 ->
+ * round_half_even(x / s-) clamped to [-qa, 0] (a zero scale gives 0;
+ * division is IEEE fp32, correctly rounded); then, when lsb_k > 0, the k low
+ * bits of the code's magnitude are cleared with the sign kept.
+ *   X             : DEVICE [M,K], fp32 or bf16 per the plan.
+ *   M             : rows, >= 0 (0 enqueues nothing).
+ *   lsb_k         : 0 <= lsb_k < a_bits.
+ *   static_scales : DEVICE fp32 [2] {s+, s-}, or NULL for dynamic scales.
+ *   codes         : DEVICE out: int8 [M,K] (a_bits 8) or uint8 [M,K/2]
+ *                   packed as above (a_bits 4).
+ *   act_scales    : DEVICE out fp32 [2] {s+, s-} used for the codes.
+ */
+ql_status qlinear_quantize_act(qlinear_plan_t p, const void* X, int32_t M, int32_t lsb_k,
+                               const float* static_scales, void* codes, float* act_scales,
+                               void* stream);
+
+/*
+ * Integer GEMM of the codes against the plan's weight codes with the fp32
+ * epilogue. DUAL: acc+ = sum_k max(c,0) w, acc- = sum_k min(c,0) w (int32,
+ * exact), y = ((float)acc+ * s+ + (float)acc- * s-) * s_w[n];
+ * SYMMETRIC: y = ((float)(acc+ + acc-) * s) * s_w[n]; then y *= 1/B when the
+ * plan rotates (B = hadamard_block). All fp32 operations are rounded
+ * individually in this order (no fused multiply-add).
+ *   codes      : DEVICE, as written by qlinear_quantize_act, M rows.
+ *   act_scales : DEVICE fp32 [2].
+ *   M          : rows, >= 0; must be even when cfg = 1.
+ *   cfg        : 0 -> Y [M,N] = y.
+ *                1 -> rows [0,M/2) are conditional, [M/2,M) unconditional;
+ *                     Y [M/2,N] = yu + w * (yc - yu), with d = yc - yu,
+ *                     t = w * d, Y = yu + t rounded in that order.
+ *   w          : guidance weight (used when cfg = 1).
+ *   Y          : DEVICE fp32 out, [M,N] or [M/2,N].
+ *   acc_dbg    : NULL, or DEVICE int32 [2,M,N] out: plane 0 = acc+, plane
+ *                1 = acc- for every row (SYMMETRIC: plane 0 = acc+ + acc-,
+ *                plane 1 = 0). For parity checks; costs extra stores.
+ */
+ql_status qlinear_gemm(qlinear_plan_t p, const void* codes, const float* act_scales, int32_t M,
+                       int32_t cfg, float w, float* Y, int32_t* acc_dbg, void* stream);
+
+/*
+ * Standalone classifier-free-guidance combine ("Closing the Null Space"
+ * explainer, problem statement): for r < M/2,
+ * out[r,n] = Y[r+M/2,n] + w * (Y[r,n] - Y[r+M/2,n]), rounded as in
+ * qlinear_gemm. Y DEVICE fp32 [M,N] (M even), out DEVICE fp32 [M/2,N];
+ * out must not overlap Y.
+ */
+ql_status qlinear_cfg_combine(const float* Y, int32_t M, int32_t N, float w, float* out,
+                              void* stream);
+
+/* Message for the last non-OK status on this thread ("" if none). */
+const char* qlinear_last_error(void);
+
+/* Library version string. */
+const char* qlinear_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* QLINEAR_H */

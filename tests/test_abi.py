@@ -1,0 +1,118 @@
+"""The C-ABI library loads and exports every entry point include/qlinear.h
+declares; host-side argument checks reject bad calls before anything
+touches a GPU (these run on the CPU)."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+from bit_post_quantization_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "qlinear.h")
+
+
+def _declared():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(qlinear_\w+)\s*\(", src)))
+
+
+def test_header_declares_expected_entry_points():
+    assert _declared() == sorted(_lib.EXPORTS)
+
+
+def test_library_exports_every_declared_symbol():
+    L = _lib.load()
+    for name in _declared():
+        assert hasattr(L, name), name
+    out = subprocess.run(["nm", "-D", "--defined-only", _lib.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    exported = set(re.findall(r"\bT (qlinear_\w+)", out))
+    assert exported == set(_declared())
+
+
+def test_version_string():
+    assert "gfx950" in _lib.load().qlinear_version().decode()
+
+
+def _desc(**kw):
+    base = dict(N=64, K=128, w_bits=8, a_bits=8, hadamard_block=0, n_segments=1,
+                seg_offsets=None, w_scale_mode=2, a_scale_mode=0, x_dtype=0)
+    base.update(kw)
+    return _lib.QlDesc(**base)
+
+
+def _plan_status(d, W=0x1000):
+    L = _lib.load()
+    h = ctypes.c_void_p()
+    st = L.qlinear_plan(ctypes.byref(d) if d is not None else None, W, None, ctypes.byref(h))
+    return st, L.qlinear_last_error().decode()
+
+
+@pytest.mark.parametrize("kw,frag", [
+    (dict(N=0), "N = 0"),
+    (dict(K=8), "K = 8"),
+    (dict(K=70000), "K = 70000"),
+    (dict(w_bits=6), "w_bits"),
+    (dict(a_bits=2), "a_bits"),
+    (dict(K=48, w_bits=4), "multiple of 32"),
+    (dict(K=40), "multiple of 16"),
+    (dict(hadamard_block=48), "power of two"),
+    (dict(K=192, hadamard_block=128), "not a multiple"),
+    (dict(w_scale_mode=7), "w_scale_mode"),
+    (dict(a_scale_mode=3), "a_scale_mode"),
+    (dict(x_dtype=5), "x_dtype"),
+    (dict(n_segments=0), "n_segments"),
+    (dict(n_segments=2), "seg_offsets is NULL"),
+])
+def test_plan_rejects_bad_descriptor(kw, frag):
+    st, msg = _plan_status(_desc(**kw))
+    assert st == _lib.QL_ERR_ARG and frag in msg
+
+
+def test_plan_rejects_bad_segments():
+    for segs in ([0, 32, 32, 64], [0, 40, 30, 64], [1, 32, 64], [0, 32, 60]):
+        arr = (ctypes.c_int32 * len(segs))(*segs)
+        d = _desc(n_segments=len(segs) - 1, w_scale_mode=1,
+                  seg_offsets=ctypes.cast(arr, ctypes.POINTER(ctypes.c_int32)))
+        st, msg = _plan_status(d)
+        assert st == _lib.QL_ERR_ARG, (segs, msg)
+
+
+def test_plan_rejects_unsupported_block():
+    st, msg = _plan_status(_desc(K=512, hadamard_block=256))
+    assert st == _lib.QL_ERR_UNSUPPORTED and "256" in msg
+
+
+def test_plan_rejects_null_pointers():
+    st, _ = _plan_status(None)
+    assert st == _lib.QL_ERR_ARG
+    st, msg = _plan_status(_desc(), W=0)
+    assert st == _lib.QL_ERR_ARG and "NULL" in msg
+    st, msg = _plan_status(_desc(), W=0x1004)
+    assert st == _lib.QL_ERR_ARG and "aligned" in msg
+
+
+def test_calls_reject_null_plan():
+    L = _lib.load()
+    assert L.qlinear_quantize_act(None, 0x1000, 4, 0, None, 0x1000, 0x1000, None) == _lib.QL_ERR_ARG
+    assert L.qlinear_gemm(None, 0x1000, 0x1000, 4, 0, 1.0, 0x1000, None, None) == _lib.QL_ERR_ARG
+    assert L.qlinear_plan_weights(None, None, None, None) == _lib.QL_ERR_ARG
+    assert L.qlinear_plan_destroy(None) == _lib.QL_OK
+
+
+def test_cfg_combine_host_checks():
+    L = _lib.load()
+    assert L.qlinear_cfg_combine(0x1000, 3, 4, 4.0, 0x9000, None) == _lib.QL_ERR_ARG
+    assert "even" in L.qlinear_last_error().decode()
+    assert L.qlinear_cfg_combine(0x1000, 4, 0, 4.0, 0x9000, None) == _lib.QL_ERR_ARG
+    assert L.qlinear_cfg_combine(None, 4, 4, 4.0, 0x9000, None) == _lib.QL_ERR_ARG
+    assert L.qlinear_cfg_combine(None, 0, 4, 4.0, None, None) == _lib.QL_OK
+    # out overlapping Y
+    assert L.qlinear_cfg_combine(0x1000, 4, 4, 4.0, 0x1010, None) == _lib.QL_ERR_ARG
+    assert "overlaps" in L.qlinear_last_error().decode()
+    # empty input is a no-op and never reaches a launch
+    assert L.qlinear_cfg_combine(0x1000, 0, 4, 4.0, 0x9000, None) == _lib.QL_OK

@@ -1,0 +1,294 @@
+"""GPU parity: the HIP path through the C ABI against the CPU oracle on the
+same seeded inputs. Sizes span several tiles plus ragged tails; the
+full-size workloads are checked on sampled rows (codes in full)."""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+
+import oracle
+from tests.parity import (assert_close, assert_codes, compare_codes, say, unpack_codes)
+from workloads import configs, synth
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def torch():
+    import torch as _t
+    assert _t.cuda.is_available(), "GPU tests need a ROCm device"
+    import bit_post_quantization_amd  # noqa: F401  (fails loudly if the library is missing)
+    return _t
+
+
+def _dev(t, a):
+    return t.from_numpy(np.ascontiguousarray(a)).cuda()
+
+
+def sample_rows(M: int, cfg: bool, n: int = 48, seed: int = 0) -> np.ndarray:
+    """Seeded sample of rows (conditional rows when cfg), plus tile edges."""
+    top = M // 2 if cfg else M
+    edges = [0, 1, 15, 16, 63, 64, 127, 128, top - 1]
+    rnd = synth.random_int_codes(seed, f"rows/{M}/{cfg}", (n,), 0, 127).astype(np.int64)
+    rnd = (rnd * 7919 + np.arange(n) * 104729) % top
+    return np.unique(np.concatenate([np.array([e for e in edges if 0 <= e < top]), rnd]))
+
+
+def check_layer(torch, X, W, *, M, K, N, w_bits=8, a_bits=8, B=0, seg=None, w_scale="channel",
+                a_scale="dual", x_dtype="f32", cfg=0, guidance=4.0, lsb_k=0,
+                static_scales=None, rows=None, tag=""):
+    """Run one quantized linear on the GPU and check every stage against the oracle.
+    rows=None checks every output row."""
+    from bit_post_quantization_amd import QuantLinear
+    say(f"[case] {tag} M={M} K={K} N={N} w{w_bits}a{a_bits} B={B} seg={seg} {w_scale} "
+        f"{a_scale} {x_dtype} cfg={cfg} k={lsb_k} static={static_scales is not None}")
+    # --- plan / weights ---
+    Wd = _dev(torch, W)
+    ql = QuantLinear(Wd, w_bits=w_bits, a_bits=a_bits, hadamard_block=B, seg_offsets=seg,
+                     w_scale=w_scale, a_scale=a_scale, x_dtype=x_dtype)
+    wp = oracle.WeightPlan(W, w_bits, B=B, mode=w_scale, seg_offsets=seg)
+    wc_g, sw_g = ql.weights()
+    torch.cuda.synchronize()
+    wc_g, sw_g = wc_g.cpu().numpy(), sw_g.cpu().numpy()
+    assert np.array_equal(sw_g.view(np.uint32), wp.scales.view(np.uint32)), "weight scales"
+    assert np.array_equal(wc_g, wp.codes), "weight codes"
+    # --- activations ---
+    Xd = _dev(torch, X) if x_dtype == "f32" else _dev(torch, X.view(np.int16))
+    ss = None if static_scales is None else _dev(torch, np.asarray(static_scales, np.float32))
+    codes_d, s_d = ql.quantize(Xd, lsb_k=lsb_k, static_scales=ss)
+    torch.cuda.synchronize()
+    s_g = s_d.cpu().numpy()
+    codes_g = unpack_codes(codes_d.cpu().numpy(), K, a_bits)
+    x32 = oracle.bf16_to_f32(X) if x_dtype == "bf16" else X
+    x_rot = oracle.rotate(x32, B) if B else x32
+    s_o = (oracle.act_scales(x_rot, a_bits, a_scale) if static_scales is None
+           else np.asarray(static_scales, np.float32))
+    assert np.array_equal(s_g.view(np.uint32), s_o.view(np.uint32)), f"act scales {s_g} vs {s_o}"
+    codes_o = oracle.quantize_act(x_rot, s_o, a_bits, lsb_k)
+    st = compare_codes(codes_g, codes_o, x_rot, s_o)
+    say(f"  codes: {st}")
+    assert_codes(st)
+    # --- GEMM with accumulator dump ---
+    Mo = M // 2 if cfg else M
+    Yd = torch.empty((Mo, N), dtype=torch.float32, device="cuda")
+    dbg = torch.empty((2, M, N), dtype=torch.int32, device="cuda")
+    ql.gemm(codes_d, s_d, cfg=cfg, w=guidance, Y=Yd, acc_dbg=dbg)
+    Yd2 = torch.empty_like(Yd)
+    ql.gemm(codes_d, s_d, cfg=cfg, w=guidance, Y=Yd2)  # launch configuration without the dump
+    torch.cuda.synchronize()
+    assert torch.equal(Yd.view(torch.int32), Yd2.view(torch.int32)), "Y differs without acc dump"
+    out_rows = np.arange(Mo) if rows is None else np.asarray(rows)
+    acc_rows = np.concatenate([out_rows, out_rows + M // 2]) if cfg else out_rows
+    idx = torch.from_numpy(acc_rows).cuda()
+    accp_g = dbg[0].index_select(0, idx).cpu().numpy()
+    accn_g = dbg[1].index_select(0, idx).cpu().numpy()
+    Y_g = Yd.index_select(0, torch.from_numpy(out_rows).cuda()).cpu().numpy()
+    accp_o, accn_o = oracle.gemm_dual(codes_g, wp.codes, acc_rows)
+    if a_scale == "symmetric":
+        assert np.array_equal(accp_g.astype(np.int64), accp_o.astype(np.int64) + accn_o), "acc (sym)"
+        assert not accn_g.any()
+    else:
+        assert np.array_equal(accp_g, accp_o), "acc+"
+        assert np.array_equal(accn_g, accn_o), "acc-"
+    y_o = oracle.epilogue(accp_o, accn_o, s_g, wp.scales, B, a_scale)
+    if cfg:
+        h = out_rows.size
+        ref = oracle.cfg_combine(y_o[:h], y_o[h:], guidance)
+    else:
+        ref = y_o
+    e = assert_close(Y_g, ref, "Y")
+    exact = np.array_equal(Y_g.view(np.uint32), ref.view(np.uint32))
+    say(f"  acc exact; Y max rel err {e:.3g}; bit-exact={exact}")
+    del dbg
+    return dict(codes=st, y_rel=e, y_exact=exact)
+
+
+# ---------------------------------------------------------------- small ----
+
+def test_config1_full(torch):
+    wl = configs.WORKLOADS["c1"]
+    L = wl.layers[0]
+    X = configs.make_x(wl, L)
+    W = configs.make_w(wl, L)
+    r = check_layer(torch, X, W, M=wl.M, K=L.K, N=L.N, tag="c1")
+    assert r["y_exact"]
+
+
+GRID = [
+    # (a_bits, w_bits, B, cfg, a_scale, x_dtype, K)
+    (8, 8, 0, 0, "dual", "f32", 1056),
+    (8, 8, 0, 1, "dual", "f32", 1056),
+    (4, 4, 0, 1, "dual", "f32", 1056),
+    (4, 4, 32, 1, "dual", "f32", 1056),
+    (8, 4, 0, 0, "dual", "bf16", 1056),
+    (4, 8, 0, 0, "dual", "f32", 1056),
+    (8, 8, 128, 1, "dual", "f32", 640),
+    (4, 4, 128, 0, "symmetric", "f32", 640),
+    (8, 8, 0, 1, "symmetric", "bf16", 1056),
+    (8, 8, 64, 0, "dual", "bf16", 1088),
+]
+
+
+@pytest.mark.parametrize("a_bits,w_bits,B,cfg,a_scale,x_dtype,K", GRID)
+def test_grid_full_rows(torch, a_bits, w_bits, B, cfg, a_scale, x_dtype, K):
+    M, N = 302, 200
+    name = f"grid/{a_bits}{w_bits}{B}{cfg}{a_scale}{x_dtype}{K}"
+    X = synth.gelu_with_outliers(1, name + "/X", M, K)
+    if x_dtype == "bf16":
+        X = synth.f32_to_bf16_bits(X)
+    W = synth.weight_normal(1, name + "/W", N, K)
+    check_layer(torch, X, W, M=M, K=K, N=N, w_bits=w_bits, a_bits=a_bits, B=B, cfg=cfg,
+                a_scale=a_scale, x_dtype=x_dtype, tag=name)
+
+
+@pytest.mark.parametrize("lsb_k,a_bits", [(2, 8), (4, 8), (7, 8), (1, 4), (3, 4)])
+def test_lsb_truncation(torch, lsb_k, a_bits):
+    M, K, N = 130, 512, 96
+    X = synth.silu_normal(2, f"lsb/{lsb_k}{a_bits}", M, K)
+    W = synth.weight_normal(2, f"lsb/W{lsb_k}{a_bits}", N, K)
+    check_layer(torch, X, W, M=M, K=K, N=N, a_bits=a_bits, w_bits=a_bits, cfg=1, lsb_k=lsb_k,
+                tag=f"lsb{lsb_k}")
+
+
+@pytest.mark.parametrize("w_scale,seg", [
+    ("segment", [0, 64, 128, 192]), ("tensor", None), ("segment", [0, 10, 11, 100, 192]),
+    ("segment", list(range(0, 193, 1)))])
+def test_segments(torch, w_scale, seg):
+    M, K, N = 200, 256, 192
+    X = synth.bf16_normal(3, f"seg/{len(seg or [])}", M, K)
+    W = synth.weight_normal(3, f"seg/W{len(seg or [])}", N, K)
+    check_layer(torch, X, W, M=M, K=K, N=N, w_bits=4, a_bits=8, seg=seg, w_scale=w_scale,
+                x_dtype="bf16", tag="seg")
+
+
+def test_static_scales(torch):
+    M, K, N = 64, 256, 80
+    X = synth.silu_normal(4, "static/X", M, K)
+    W = synth.weight_normal(4, "static/W", N, K)
+    check_layer(torch, X, W, M=M, K=K, N=N, static_scales=[0.01, 0.002], tag="static")
+    check_layer(torch, X, W, M=M, K=K, N=N, a_bits=4, w_bits=4, static_scales=[0.5, 0.0],
+                tag="static-zero-neg")
+
+
+@pytest.mark.parametrize("M,K,N,a_bits,w_bits,cfg", [
+    (2, 16, 1, 8, 8, 1), (1, 32, 3, 4, 4, 0), (129, 64, 129, 8, 8, 0), (256, 128, 256, 8, 4, 1),
+    (4, 1024, 1, 4, 8, 1)])
+def test_small_and_ragged_shapes(torch, M, K, N, a_bits, w_bits, cfg):
+    X = synth.gelu_normal(5, f"shape/{M}{K}{N}", M, K)
+    W = synth.weight_normal(5, f"shape/W{M}{K}{N}", N, K)
+    check_layer(torch, X, W, M=M, K=K, N=N, a_bits=a_bits, w_bits=w_bits, cfg=cfg, tag="shape")
+
+
+def test_degenerate_inputs(torch):
+    M, K, N = 64, 128, 64
+    W = synth.weight_normal(6, "deg/W", N, K)
+    pos = np.abs(synth.silu_normal(6, "deg/pos", M, K)) + np.float32(0.01)
+    check_layer(torch, pos, W, M=M, K=K, N=N, tag="all-positive")       # s- = 0
+    check_layer(torch, -pos, W, M=M, K=K, N=N, cfg=1, tag="all-negative")  # s+ = 0
+    z = np.zeros((M, K), np.float32)
+    z[::3, ::5] = -0.0
+    r = check_layer(torch, z, W, M=M, K=K, N=N, tag="all-zero")
+    assert r["y_exact"]
+    Wz = np.zeros((N, K), np.float32)
+    check_layer(torch, pos, Wz, M=M, K=K, N=N, tag="zero-weights")
+
+
+def test_empty_input_is_noop(torch):
+    from bit_post_quantization_amd import QuantLinear
+    W = _dev(torch, synth.weight_normal(7, "empty/W", 32, 64))
+    ql = QuantLinear(W)
+    X = torch.zeros((0, 64), dtype=torch.float32, device="cuda")
+    codes, s = ql.quantize(X)
+    Y = ql.gemm(codes, s, cfg=1)
+    torch.cuda.synchronize()
+    assert codes.shape == (0, 64) and Y.shape == (0, 32)
+
+
+def test_repeated_dynamic_calls_reset_workspace(torch):
+    # The reduction workspace must come back to zero after every call: a
+    # second tensor with a smaller range must get its own scales.
+    from bit_post_quantization_amd import QuantLinear
+    K, N = 256, 64
+    ql = QuantLinear(_dev(torch, synth.weight_normal(8, "rep/W", N, K)))
+    for i, mult in enumerate([10.0, 1.0, 0.1, 5.0]):
+        X = (synth.gelu_normal(8, f"rep/X{i}", 97, K) * np.float32(mult)).astype(np.float32)
+        codes, s = ql.quantize(_dev(torch, X))
+        torch.cuda.synchronize()
+        assert np.array_equal(s.cpu().numpy(), oracle.act_scales(X, 8)), i
+
+
+def test_cfg_combine_standalone(torch):
+    from bit_post_quantization_amd import qlinear_cfg_combine
+    for M, N in [(302, 77), (2, 1), (4096, 1152)]:
+        Y = synth.normal_f64(9, f"cfg/{M}{N}", (M, N)).astype(np.float32)
+        Yd = _dev(torch, Y)
+        out = torch.empty((M // 2, N), dtype=torch.float32, device="cuda")
+        qlinear_cfg_combine(Yd, M, N, 4.0, out)
+        torch.cuda.synchronize()
+        ref = oracle.cfg_combine(Y[: M // 2], Y[M // 2:], 4.0)
+        assert np.array_equal(out.cpu().numpy().view(np.uint32), ref.view(np.uint32))
+
+
+def test_gpu_argument_errors(torch):
+    from bit_post_quantization_amd import QLError, QuantLinear, qlinear_gemm, qlinear_quantize_act
+    ql = QuantLinear(_dev(torch, synth.weight_normal(10, "err/W", 32, 64)))
+    X = torch.zeros((5, 64), dtype=torch.float32, device="cuda")
+    codes = torch.empty((5, 64), dtype=torch.int8, device="cuda")
+    s = torch.empty(2, dtype=torch.float32, device="cuda")
+    with pytest.raises(QLError):
+        qlinear_quantize_act(ql.plan, X, 5, 8, None, codes, s)
+    with pytest.raises(QLError):
+        qlinear_quantize_act(ql.plan, X, -1, 0, None, codes, s)
+    Y = torch.empty((5, 32), dtype=torch.float32, device="cuda")
+    with pytest.raises(QLError):
+        qlinear_gemm(ql.plan, codes, s, 5, 1, 4.0, Y)  # odd M with CFG
+    with pytest.raises(QLError):
+        qlinear_gemm(ql.plan, codes, s, 4, 2, 4.0, Y)  # bad cfg flag
+
+
+# ------------------------------------------------------------ full size ----
+
+def _run_workload_layer(torch, key, li, rows_n=48):
+    wl = configs.WORKLOADS[key]
+    L = wl.layers[li]
+    X = configs.make_x(wl, L)
+    W = configs.make_w(wl, L)
+    rows = sample_rows(wl.M, L.cfg, rows_n, seed=li)
+    return check_layer(torch, X, W, M=wl.M, K=L.K, N=L.N, w_bits=L.w_bits, a_bits=L.a_bits,
+                       B=L.hadamard_block, seg=None if L.seg_offsets() is None else L.seg_offsets().tolist(),
+                       w_scale=L.w_scale, a_scale=L.a_scale, x_dtype=L.x_dtype, cfg=int(L.cfg),
+                       guidance=L.guidance, rows=rows, tag=f"{key}/{L.name}")
+
+
+@pytest.mark.timeout(600)
+@pytest.mark.parametrize("li", range(4))
+def test_config2_dit_w8a8_cfg(torch, li):
+    _run_workload_layer(torch, "c2", li)
+
+
+@pytest.mark.timeout(600)
+@pytest.mark.parametrize("li", range(4))
+def test_config3_dit_w4a4_hadamard(torch, li):
+    _run_workload_layer(torch, "c3", li)
+
+
+@pytest.mark.timeout(900)
+@pytest.mark.parametrize("li", range(4))
+def test_config4_mmdit_segments(torch, li):
+    _run_workload_layer(torch, "c4", li, rows_n=24)
+
+
+@pytest.mark.timeout(900)
+def test_config5_tasq_steps(torch):
+    # Every layer of one block over several steps of the schedule, plus the
+    # first layer of every block at step 0 (the full sweep is a benchmark).
+    wl = configs.WORKLOADS["c5"]
+    sched = configs.c5_schedule()
+    cases = [(t, li) for t in (0, 1, 49) for li in range(4)] + [(0, 4 * b) for b in range(1, 28, 9)]
+    for t, li in cases:
+        L = wl.layers[li]
+        X = configs.make_x(wl, L, step=t)
+        W = configs.make_w(wl, L)
+        rows = sample_rows(wl.M, True, 16, seed=t * 1000 + li)
+        check_layer(torch, X, W, M=wl.M, K=L.K, N=L.N, cfg=1, guidance=L.guidance,
+                    lsb_k=int(sched[t, li]), rows=rows, tag=f"c5/t{t}/{L.name}")
