@@ -29,9 +29,16 @@ def hipcc() -> str:
     return p
 
 
+# The GEMM keeps its MFMA accumulators in architectural VGPRs: with AGPR
+# accumulators the register allocator rotates them through copies inside the
+# unrolled K loop.
+EXTRA = {"k_gemm.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
+
+
 def _compile(src: str) -> str:
     obj = os.path.join(OBJ, os.path.splitext(src)[0] + ".o")
-    cmd = [hipcc()] + FLAGS + ["-x", "hip", "-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = ([hipcc()] + FLAGS + EXTRA.get(src, [])
+           + ["-x", "hip", "-c", os.path.join(CSRC, src), "-o", obj])
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed for {src}:\n{r.stderr}")

@@ -268,6 +268,8 @@ ql_status qlinear_gemm(qlinear_plan_t p, const void* codes, const float* act_sca
   g.Mh = cfg ? M / 2 : M;
   g.lda = p->d.a_bits == 4 ? p->d.K / 2 : p->d.K;
   g.ldw = p->d.w_bits == 4 ? p->d.K / 2 : p->d.K;
+  if ((int64_t)M * g.lda >= ((int64_t)1 << 31) || (int64_t)g.N * g.ldw >= ((int64_t)1 << 31))
+    return fail(QL_ERR_UNSUPPORTED, "codes or weights of 2 GiB or more (M = %d)", M);
   g.guidance = w;
   g.inv_b = p->d.hadamard_block ? 1.0f / (float)p->d.hadamard_block : 1.0f;
   hipError_t e = ql::launch_gemm(g, p->d.a_bits == 4, p->d.w_bits == 4,
