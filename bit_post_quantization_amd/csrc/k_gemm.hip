@@ -13,25 +13,33 @@
 //    registers into its two polarity planes (byte sign masks) and both are
 //    multiplied by the same weight fragment into two accumulator sets: the
 //    batch-2 GEMM of the method shares every weight fragment it reads.
-//  * Tile 128 rows x (16*NB) columns, 4 waves of 32 rows each, one workgroup
-//    per CU. NB = 9 (144 columns) makes the DiT-XL/2 widths (1152, 3456,
-//    4608 = 8, 24, 32 x 144) give exactly 1, 3 or 4 tiles per CU at M = 4096.
-//  * Operands move HBM -> LDS by buffer_load ... lds (no VGPR staging) into
-//    a ring of kStages K-steps, issued kStages-1 steps ahead. The buffer
-//    resource's range check turns every out-of-range row or K-chunk into
-//    zeros, so ragged M, N and K need no special path.
-//  * LDS holds operands in fragment order: the 16 bytes lane l feeds to the
-//    MFMA sit at lane*16, so fragment reads are linear and conflict-free.
-//    4-bit codes stay packed in LDS (half the bytes) and are unpacked on the
-//    LDS -> register path, each code multiplied by 16 (nibble placed in the
-//    high half of its byte: two ANDs, a shift, two byte permutes); the
-//    accumulators are shifted back exactly at the end.
-//  * CFG pairing: a tile holds 64 conditional rows and their 64
-//    unconditional partners; a wave's fragment 0 is 16 conditional rows and
-//    fragment 1 their partners, so a lane holds both accumulators of a pair
-//    in the same register slot and combines them with no data exchange.
-//  * Workgroups are mapped to tiles so that each XCD (workgroup id mod 8)
-//    works on one contiguous band of tiles, which share rows in its L2.
+//  * Output tile 128 rows x (16*NB) columns, NB = 9 (144 columns) when it
+//    divides N: the DiT-XL/2 widths 1152, 3456, 4608 are 8, 24, 32 x 144, so
+//    at M = 4096 (CFG pairs) the tile counts are exact multiples of 256 CUs.
+//  * 8 waves per workgroup (2 per SIMD, so one wave's waits overlap the
+//    other's MFMAs): wave w owns 32 rows (row band w % 4) and one of two
+//    column groups (w / 4) of ceil(NB/2) / floor(NB/2) fragments; the two
+//    waves sharing a SIMD carry NB fragments together.
+//  * Both operands go HBM -> LDS by buffer_load ... lds (no VGPR staging)
+//    into a ring of 6 K-steps, 5 steps ahead of the MFMAs; each fragment is
+//    loaded once per workgroup by one wave (17 loads per K-step for the
+//    whole workgroup). The DMA lanes read whole 64-byte row segments
+//    (coalesced) and the LDS image is XOR-swizzled so that the MFMA
+//    operand reads are bank-conflict free.
+//  * Persistent workgroups: each one walks its tiles as one continuous
+//    stream of K-steps, so the loads of the next tile overlap the epilogue of
+//    the current one. Workgroups (whose id mod 8 is their XCD) get bands of
+//    consecutive tiles that share rows in that XCD's L2.
+//  * Every out-of-range row or K-chunk is read as zero by the buffer range
+//    check, so ragged M, N and K need no special path; K is padded to a
+//    multiple of 6 steps with such zero steps.
+//  * 4-bit codes stay packed through memory and LDS and are unpacked on the
+//    way into the MFMA, each code multiplied by 16 (nibble placed in the high
+//    half of its byte: two ANDs, a shift, two byte permutes); accumulators
+//    are shifted back exactly in the epilogue.
+//  * CFG pairing: a row band is 16 conditional rows and their 16
+//    unconditional partners (fragments 0 and 1), so a lane holds both
+//    accumulators of a pair in the same register slot.
 #include <type_traits>
 
 #include "ql_device.h"
@@ -42,34 +50,17 @@ namespace ql {
 namespace {
 
 typedef int v4i __attribute__((ext_vector_type(4)));
+typedef unsigned v4u __attribute__((ext_vector_type(4)));
+typedef unsigned v2u __attribute__((ext_vector_type(2)));
 typedef __attribute__((address_space(3))) void lds_void;
 template <int V>
 using IC = std::integral_constant<int, V>;
 
-constexpr int kThreads = 256;
-constexpr int kWaves = 4;
-constexpr int BK = 64;        // K elements per ring stage
-constexpr int kStages = 6;    // ring depth
+constexpr int kThreads = 512;
+constexpr int kWaves = 8;
+constexpr int BK = 64;                  // K elements per ring stage
+constexpr int kStages = 6;              // ring depth (= unroll of the K loop)
 constexpr unsigned kOOB = 0x80000000u;  // offset beyond every buffer: loads return 0
-
-template <bool P4>
-struct Op {
-  static constexpr int kFragBytes = P4 ? 512 : 1024;  // one 16 x 64 fragment
-  static constexpr int kLoads = P4 ? 2 : 1;           // DMA instructions per fragment
-};
-
-template <bool A4, bool W4, int NB>
-struct Layout {
-  static constexpr int kAFrags = 8;                       // 128 rows
-  static constexpr int kWPerWave = (NB + kWaves - 1) / kWaves;
-  static constexpr int kABytes = kAFrags * Op<A4>::kFragBytes;
-  static constexpr int kWBytes = NB * Op<W4>::kFragBytes;
-  static constexpr int kStage = kABytes + kWBytes;
-  static constexpr int kSink = Op<W4>::kFragBytes;       // target of padding loads
-  static constexpr int kLds = kStages * kStage + kSink;
-  // DMA instructions one wave issues per stage (same for every wave)
-  static constexpr int kLoadsPerStage = 2 * Op<A4>::kLoads + kWPerWave * Op<W4>::kLoads;
-};
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes,
@@ -83,56 +74,94 @@ __device__ __forceinline__ void wait_vmcnt() {
   __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
 }
 
-// One fragment (16 rows x 64 K) from global into LDS at `dst` (wave-uniform).
-// row_off: byte offset of this lane's row, or kOOB. Lane l covers K-chunk
-// l/16 (16 elements) of row l%16.
+// LDS image of one 16-row x 64-K fragment and the DMA that fills it.
+//
+// int8 (1 KB): one 16-byte DMA per lane. Lane p loads row p/4, chunk
+// (p%4) ^ ((p/16)%4) of the row's 64 bytes, so each group of 4 consecutive
+// lanes reads one contiguous 64-byte row segment (coalesced) and lane p's
+// bytes land at p*16. An MFMA lane l (row l%16, K-chunk l/16) then reads
+// position 4*(l%16) + ((l/16) ^ ((l%16)/4)): the 16 lanes that read together
+// hit 16 distinct 16-byte bank groups.
+//
+// packed 4-bit (512 B): two 4-byte DMAs per lane in MFMA order (lane l: row
+// l%16, bytes 8*(l/16) .. +8 of the row's 32), read back as two dwords.
 template <bool P4>
-__device__ __forceinline__ void dma_frag(__amdgpu_buffer_rsrc_t r, uint8_t* dst, unsigned row_off,
-                                         int k0, int K, int lane) {
-  const int kk = k0 + 16 * (lane >> 4);
-  const bool ok = row_off != kOOB && kk < K;
-  if constexpr (P4) {
-    const unsigned v = ok ? row_off + (unsigned)(kk >> 1) : kOOB;
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)dst, 4, v, 0, 0, 0);
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)(dst + 256), 4, v + 4u, 0, 0, 0);
-  } else {
-    const unsigned v = ok ? row_off + (unsigned)kk : kOOB;
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)dst, 16, v, 0, 0, 0);
-  }
-}
-
-// Raw fragment data of one lane: int8 -> 4 dwords, 4-bit -> 2 dwords.
-template <bool P4>
-struct Raw {
+struct Frag {
   uint32_t d[P4 ? 2 : 4];
 };
 
 template <bool P4>
-__device__ __forceinline__ void read_frag(Raw<P4>& f, const uint8_t* src, int lane) {
-  if constexpr (P4) {
-    f.d[0] = *reinterpret_cast<const uint32_t*>(src + lane * 4);
-    f.d[1] = *reinterpret_cast<const uint32_t*>(src + 256 + lane * 4);
-  } else {
-    const uint4 v = *reinterpret_cast<const uint4*>(src + lane * 16);
-    f.d[0] = v.x;
-    f.d[1] = v.y;
-    f.d[2] = v.z;
-    f.d[3] = v.w;
+struct FragIO {
+  static constexpr int kBytes = P4 ? 512 : 1024;
+  static constexpr int kLoads = P4 ? 2 : 1;
+  // Row (0..15) inside the fragment that DMA lane p loads.
+  __device__ static __forceinline__ int dma_row(int p) { return P4 ? (p & 15) : (p >> 2); }
+  // K-chunk (16 elements) of the 64-element step that DMA lane p loads.
+  __device__ static __forceinline__ int dma_chunk(int p) {
+    return P4 ? (p >> 4) : ((p & 3) ^ ((p >> 4) & 3));
   }
-}
+  // Byte offset of that chunk inside a row's step.
+  __device__ static __forceinline__ unsigned chunk_off(int p) {
+    return (unsigned)dma_chunk(p) * (P4 ? 8u : 16u);
+  }
+  // Where MFMA lane l finds its operand inside the fragment.
+  __device__ static __forceinline__ int read_off(int l) {
+    if constexpr (P4) return l * 4;
+    const int r = l & 15;
+    return (4 * r + ((l >> 4) ^ (r >> 2))) * 16;
+  }
+  // DMA of this lane's part of the fragment into LDS at `dst` (wave-uniform).
+  __device__ static __forceinline__ void dma(__amdgpu_buffer_rsrc_t r, uint8_t* dst, unsigned voff,
+                                             unsigned soff) {
+    if constexpr (P4) {
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)dst, 4, voff, soff, 0, 0);
+      // (+4 bytes through the scalar offset: an instruction offset would also
+      // move the LDS destination)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)(dst + 256), 4, voff, soff + 4u, 0, 0);
+    } else {
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)dst, 16, voff, soff, 0, 0);
+    }
+  }
+  __device__ static __forceinline__ void read(Frag<P4>& f, const uint8_t* frag, int roff) {
+    if constexpr (P4) {
+      f.d[0] = *reinterpret_cast<const uint32_t*>(frag + roff);
+      f.d[1] = *reinterpret_cast<const uint32_t*>(frag + 256 + roff);
+    } else {
+      const uint4 v = *reinterpret_cast<const uint4*>(frag + roff);
+      f.d[0] = v.x;
+      f.d[1] = v.y;
+      f.d[2] = v.z;
+      f.d[3] = v.w;
+    }
+  }
+};
+
+template <bool A4, bool W4, int NB>
+struct Layout {
+  static constexpr int kNB0 = (NB + 1) / 2;  // weight fragments of column group 0
+  static constexpr int kNB1 = NB / 2;        // weight fragments of column group 1
+  static constexpr int kAFrags = 8;          // 128 rows
+  static constexpr int kABytes = kAFrags * FragIO<A4>::kBytes;
+  static constexpr int kStage = kABytes + NB * FragIO<W4>::kBytes;
+  // DMA: wave w moves activation fragment w and weight fragment w, and waves
+  // w < NB - 8 also weight fragment w + 8.
+  static_assert(NB >= 8 && NB <= 16, "fragment distribution");
+  static constexpr int kOpsLow = FragIO<A4>::kLoads + 2 * FragIO<W4>::kLoads;  // waves < NB-8
+  static constexpr int kOpsHigh = FragIO<A4>::kLoads + FragIO<W4>::kLoads;     // the others
+};
 
 // MFMA operand (16 int8 in natural K order) from raw fragment data.
 template <bool P4>
-__device__ __forceinline__ v4i operand(const Raw<P4>& f) {
+__device__ __forceinline__ v4i operand(const Frag<P4>& f) {
   v4i o;
   if constexpr (P4) {
-    uint32_t a, b, c, d;
+    uint32_t a, b, c, e;
     unpack4_x16(f.d[0], a, b);
-    unpack4_x16(f.d[1], c, d);
+    unpack4_x16(f.d[1], c, e);
     o[0] = (int)a;
     o[1] = (int)b;
     o[2] = (int)c;
-    o[3] = (int)d;
+    o[3] = (int)e;
   } else {
     o[0] = (int)f.d[0];
     o[1] = (int)f.d[1];
@@ -142,14 +171,12 @@ __device__ __forceinline__ v4i operand(const Raw<P4>& f) {
   return o;
 }
 
-__device__ __forceinline__ void split(v4i c, v4i& p, v4i& n) {
+// Non-negative polarity plane of an operand (negative bytes zeroed).
+__device__ __forceinline__ v4i positive(v4i c) {
+  v4i p;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    uint32_t pp, nn;
-    split_polarity((uint32_t)c[i], pp, nn);
-    p[i] = (int)pp;
-    n[i] = (int)nn;
-  }
+  for (int i = 0; i < 4; ++i) p[i] = (int)pos_plane((uint32_t)c[i]);
+  return p;
 }
 
 __device__ __forceinline__ v4i mfma(v4i a, v4i b, v4i c) {
@@ -170,12 +197,39 @@ __device__ __forceinline__ float epi(int accp, int accn, float sp, float sn, flo
   return __fmul_rn(y, inv_b);
 }
 
-template <bool A4, bool W4, bool SYM, bool CFG, bool DBG, int NB>
+// Tiles of workgroup b: XCD-banded when both counts divide by 8, else strided.
+struct TileList {
+  int first, stride, count;
+  __device__ __forceinline__ int at(int i) const { return first + i * stride; }
+};
+
+__device__ __forceinline__ TileList my_tiles(int T) {
+  const int G = gridDim.x, b = blockIdx.x;
+  TileList L;
+  if ((G & 7) == 0 && (T & 7) == 0) {
+    const int x = b & 7, j = b >> 3, per_x = G >> 3, band = T >> 3;
+    L.first = x * band + j;
+    L.stride = per_x;
+    L.count = j < band ? (band - j + per_x - 1) / per_x : 0;
+  } else {
+    L.first = b;
+    L.stride = G;
+    L.count = b < T ? (T - b + G - 1) / G : 0;
+  }
+  return L;
+}
+
+template <bool A4, bool W4, bool SYM, bool CFG, int NB>
 __global__ __launch_bounds__(kThreads, 1) void k2_gemm(GemmArgs g) {
   using Lay = Layout<A4, W4, NB>;
-  constexpr int NP = SYM ? 1 : 2;                       // accumulator planes
-  constexpr int SHIFT = (A4 ? 4 : 0) + (W4 ? 4 : 0);    // undo the x16 unpack
+  using IA = FragIO<A4>;
+  using IW = FragIO<W4>;
+  constexpr int NP = SYM ? 1 : 2;                     // accumulator planes
+  constexpr int SHIFT = (A4 ? 4 : 0) + (W4 ? 4 : 0);  // undo the x16 unpack
   constexpr int BN = 16 * NB;
+  constexpr int NBG = Lay::kNB0;                      // weight fragment slots per wave
+  constexpr int RPT = CFG ? 64 : 128;                 // output rows per tile
+
   // One LDS object per ring stage: the compiler tracks DMA -> LDS writes per
   // object, so a fragment read waits only for the DMA of its own stage.
   __shared__ __attribute__((aligned(16))) uint8_t st0[Lay::kStage];
@@ -184,163 +238,40 @@ __global__ __launch_bounds__(kThreads, 1) void k2_gemm(GemmArgs g) {
   __shared__ __attribute__((aligned(16))) uint8_t st3[Lay::kStage];
   __shared__ __attribute__((aligned(16))) uint8_t st4[Lay::kStage];
   __shared__ __attribute__((aligned(16))) uint8_t st5[Lay::kStage];
-  __shared__ __attribute__((aligned(16))) uint8_t sink[Lay::kSink];
   static_assert(kStages == 6, "one LDS object per stage");
   uint8_t* const slots[kStages] = {st0, st1, st2, st3, st4, st5};
 
   const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // uniform
+  const int band = wave & 3;          // row band: 32 rows of the tile
+  const int cg = wave >> 2;           // column group
+  const int j0 = cg ? Lay::kNB0 : 0;  // first weight fragment of this wave
+  const int nbw = cg ? Lay::kNB1 : Lay::kNB0;
+  const bool two_w = wave < NB - 8;   // this wave also moves weight fragment w + 8
 
-  // ---- tile of this workgroup (XCD-banded order) ----
-  const int rows = CFG ? g.Mh : g.M;
-  const int rt = (rows + (CFG ? 63 : 127)) / (CFG ? 64 : 128);
   const int ct = (g.N + BN - 1) / BN;
-  const int T = rt * ct;
-  int t = blockIdx.x;
-  if ((T & 7) == 0) t = (t & 7) * (T >> 3) + (t >> 3);
-  const int tr = t / ct, tc = t - tr * ct;
-  const int m0 = tr * (CFG ? 64 : 128);
-  const int n0 = tc * BN;
+  const int T = (((CFG ? g.Mh : g.M) + RPT - 1) / RPT) * ct;
+  const TileList tl = my_tiles(T);
+  if (tl.count == 0) return;
 
-  // ---- per-lane row offsets for this wave's DMA work ----
-  const int i16 = lane & 15;
-  unsigned aoff[2];
-#pragma unroll
-  for (int fi = 0; fi < 2; ++fi) {
-    const int f = 2 * wave + fi;
-    int grow;
-    bool ok;
-    if constexpr (CFG) {
-      const int crow = m0 + 16 * (f >> 1) + i16;
-      ok = crow < g.Mh;
-      grow = crow + (f & 1) * g.Mh;
-    } else {
-      grow = m0 + 16 * f + i16;
-      ok = grow < g.M;
-    }
-    aoff[fi] = ok ? (unsigned)grow * (unsigned)g.lda : kOOB;
-  }
-  unsigned woff[Lay::kWPerWave];
-#pragma unroll
-  for (int i = 0; i < Lay::kWPerWave; ++i) {
-    const int j = wave + kWaves * i;
-    const int n = n0 + 16 * j + i16;
-    woff[i] = (j < NB && n < g.N) ? (unsigned)n * (unsigned)g.ldw : kOOB;
-  }
+  const int nk = (g.K + BK - 1) / BK;
+  const int nkp = (nk + kStages - 1) / kStages * kStages;  // padded with zero steps
+  const int total = tl.count * nkp;
+
   const __amdgpu_buffer_rsrc_t ra = make_rsrc(g.A, (uint32_t)((int64_t)g.M * g.lda));
   const __amdgpu_buffer_rsrc_t rw = make_rsrc(g.W, (uint32_t)((int64_t)g.N * g.ldw));
 
-  auto issue = [&](int s, uint8_t* slot) {
-    const int k0 = s * BK;
-#pragma unroll
-    for (int fi = 0; fi < 2; ++fi)
-      dma_frag<A4>(ra, slot + (2 * wave + fi) * Op<A4>::kFragBytes, aoff[fi], k0, g.K, lane);
-#pragma unroll
-    for (int i = 0; i < Lay::kWPerWave; ++i) {
-      const int j = wave + kWaves * i;
-      uint8_t* dst = j < NB ? slot + Lay::kABytes + j * Op<W4>::kFragBytes
-                            : sink;  // padding load
-      dma_frag<W4>(rw, dst, woff[i], k0, g.K, lane);
-    }
+  auto coords = [&](int ti, int& m0, int& n0) {
+    const int t = tl.at(ti);
+    const int tr = t / ct;
+    m0 = tr * RPT;
+    n0 = (t - tr * ct) * BN;
   };
 
-  struct Frags {
-    Raw<A4> a[2];
-    Raw<W4> w[NB];
-  };
-  auto read_all = [&](Frags& F, const uint8_t* slot) {
-#pragma unroll
-    for (int fi = 0; fi < 2; ++fi) read_frag<A4>(F.a[fi], slot + (2 * wave + fi) * Op<A4>::kFragBytes, lane);
-#pragma unroll
-    for (int j = 0; j < NB; ++j) read_frag<W4>(F.w[j], slot + Lay::kABytes + j * Op<W4>::kFragBytes, lane);
-  };
-
-  v4i acc[NP][2][NB];
-#pragma unroll
-  for (int p = 0; p < NP; ++p)
-#pragma unroll
-    for (int fi = 0; fi < 2; ++fi)
-#pragma unroll
-      for (int j = 0; j < NB; ++j) acc[p][fi][j] = v4i{0, 0, 0, 0};
-
-  auto compute = [&](const Frags& F) {
-#pragma unroll
-    for (int fi = 0; fi < 2; ++fi) {
-      const v4i a = operand<A4>(F.a[fi]);
-      if constexpr (SYM) {
-#pragma unroll
-        for (int j = 0; j < NB; ++j) acc[0][fi][j] = mfma(a, operand<W4>(F.w[j]), acc[0][fi][j]);
-      } else {
-        v4i ap, an;
-        split(a, ap, an);
-#pragma unroll
-        for (int j = 0; j < NB; ++j) {
-          const v4i b = operand<W4>(F.w[j]);
-          acc[0][fi][j] = mfma(ap, b, acc[0][fi][j]);
-          acc[1][fi][j] = mfma(an, b, acc[1][fi][j]);
-        }
-      }
-    }
-  };
-
-  const int nk = (g.K + BK - 1) / BK;
-  // prologue: stages 0 .. kStages-2 in flight, stage 0 landed
-#pragma unroll
-  for (int s = 0; s < kStages - 1; ++s)
-    if (s < nk) issue(s, slots[s]);
-  if (nk >= kStages - 1)
-    wait_vmcnt<(kStages - 2) * Lay::kLoadsPerStage>();
-  else
-    wait_vmcnt<0>();
-  __builtin_amdgcn_s_barrier();
-  Frags F[2];
-  read_all(F[0], slots[0]);
-
-  // One K step: wait for stage k+1, barrier, refill the ring, prefetch the
-  // fragments of stage k+1, run the MFMAs of stage k. u = k % kStages is a
-  // compile-time constant at every call site (the loops below are unrolled
-  // by the ring depth), so slots and fragment buffers are static.
-  auto step = [&](int k, auto uc) {
-    constexpr int u = decltype(uc)::value;
-    if (k + kStages - 2 < nk)
-      wait_vmcnt<(kStages - 3) * Lay::kLoadsPerStage>();
-    else
-      wait_vmcnt<0>();
-    __builtin_amdgcn_s_barrier();  // stage k+1 visible to all; slot of k-1 free
-    if (k + kStages - 1 < nk) issue(k + kStages - 1, slots[(u + kStages - 1) % kStages]);
-    // (on the last step this reads a stale slot; the values are never used)
-    read_all(F[(u + 1) & 1], slots[(u + 1) % kStages]);
-    compute(F[u & 1]);
-  };
-  int kb = 0;
-  for (; kb + kStages <= nk; kb += kStages) {
-    step(kb + 0, IC<0>{});
-    step(kb + 1, IC<1>{});
-    step(kb + 2, IC<2>{});
-    step(kb + 3, IC<3>{});
-    step(kb + 4, IC<4>{});
-    step(kb + 5, IC<5>{});
-  }
-  if (kb + 0 < nk) step(kb + 0, IC<0>{});
-  if (kb + 1 < nk) step(kb + 1, IC<1>{});
-  if (kb + 2 < nk) step(kb + 2, IC<2>{});
-  if (kb + 3 < nk) step(kb + 3, IC<3>{});
-  if (kb + 4 < nk) step(kb + 4, IC<4>{});
-
-  // ---- epilogue ----
-  const float sp = g.act_scales[0];
-  const float sn = g.act_scales[1];
-  const int rsub = (lane >> 4) * 4;
-  float sw[NB];
-  int col[NB];
-#pragma unroll
-  for (int j = 0; j < NB; ++j) {
-    col[j] = n0 + 16 * j + i16;
-    sw[j] = col[j] < g.N ? g.w_scales[col[j]] : 0.0f;
-  }
-
-  auto grow_of = [&](int fi, int i, bool& ok) {
-    const int f = 2 * wave + fi;
+  // Global row of row i (0..15) of activation fragment f (0..7) of a tile:
+  // fragment f belongs to row band f/2; with CFG, fragment 2b holds 16
+  // conditional rows and 2b+1 their unconditional partners.
+  auto a_row = [&](int m0, int f, int i, bool& ok) {
     if constexpr (CFG) {
       const int crow = m0 + 16 * (f >> 1) + i;
       ok = crow < g.Mh;
@@ -352,72 +283,250 @@ __global__ __launch_bounds__(kThreads, 1) void k2_gemm(GemmArgs g) {
     }
   };
 
-  if constexpr (DBG) {
-    const int64_t plane = (int64_t)g.M * g.N;
-#pragma unroll
-    for (int fi = 0; fi < 2; ++fi)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        bool ok;
-        const int grow = grow_of(fi, rsub + r, ok);
-        if (!ok) continue;
-#pragma unroll
-        for (int j = 0; j < NB; ++j) {
-          if (col[j] >= g.N) continue;
-          const int64_t e = (int64_t)grow * g.N + col[j];
-          g.dbg[e] = acc[0][fi][j][r] >> SHIFT;
-          g.dbg[plane + e] = SYM ? 0 : (acc[NP - 1][fi][j][r] >> SHIFT);
-        }
-      }
-  }
+  // Load stream position (kStages-1 steps ahead of the MFMAs) and this lane's
+  // DMA row offsets for the stream's tile; the K offset of a step goes into
+  // the scalar operand of the loads.
+  int iss_ti = 0, iss_k = 0;
+  unsigned av, wv0, wv1;
+  auto enter_tile = [&](int ti) {
+    int m0, n0;
+    coords(ti, m0, n0);
+    bool ok;
+    const int r = a_row(m0, wave, IA::dma_row(lane), ok);
+    av = ok ? (unsigned)r * (unsigned)g.lda + IA::chunk_off(lane) : kOOB;
+    const int n_a = n0 + 16 * wave + IW::dma_row(lane);
+    wv0 = n_a < g.N ? (unsigned)n_a * (unsigned)g.ldw + IW::chunk_off(lane) : kOOB;
+    const int n_b = n0 + 16 * (wave + 8) + IW::dma_row(lane);
+    wv1 = n_b < g.N ? (unsigned)n_b * (unsigned)g.ldw + IW::chunk_off(lane) : kOOB;
+  };
 
-  if constexpr (CFG) {
+  // Issue the stream's next stage into `slot`.
+  auto issue = [&](uint8_t* slot) {
+    const int k0 = iss_k * BK;
+    unsigned a = av, w0 = wv0, w1 = wv1;
+    unsigned sa = (unsigned)k0 / (A4 ? 2u : 1u);
+    unsigned sw = (unsigned)k0 / (W4 ? 2u : 1u);
+    if (k0 >= g.K) {
+      sa = kOOB;  // padding step: zeros
+      sw = kOOB;
+    } else if (k0 + BK > g.K) {
+      // ragged last step: chunks past K read zeros
+      a = k0 + 16 * IA::dma_chunk(lane) < g.K ? a : kOOB;
+      const bool win = k0 + 16 * IW::dma_chunk(lane) < g.K;
+      w0 = win ? w0 : kOOB;
+      w1 = win ? w1 : kOOB;
+    }
+    IA::dma(ra, slot + wave * IA::kBytes, a, sa);
+    IW::dma(rw, slot + Lay::kABytes + wave * IW::kBytes, w0, sw);
+    if (two_w) IW::dma(rw, slot + Lay::kABytes + (wave + 8) * IW::kBytes, w1, sw);
+    if (++iss_k == nkp) {
+      iss_k = 0;
+      if (++iss_ti < tl.count) enter_tile(iss_ti);
+    }
+  };
+
+  // Wait until at most N of this wave's stages are in flight (its own DMA).
+  auto wait_stages = [&](auto nc) {
+    constexpr int n = decltype(nc)::value;
+    if (two_w)
+      wait_vmcnt<n * Lay::kOpsLow>();
+    else
+      wait_vmcnt<n * Lay::kOpsHigh>();
+  };
+
+  const int roff_a = IA::read_off(lane);
+  const int roff_w = IW::read_off(lane);
+
+  struct Frags {
+    Frag<A4> a[2];
+    Frag<W4> w[NBG];
+  };
+  Frags F[2];
+  auto read_all = [&](Frags& f, const uint8_t* slot) {
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int crow = m0 + 16 * wave + rsub + r;
-      if (crow >= g.Mh) continue;
-      float* yrow = g.Y + (int64_t)crow * g.N;
+    for (int fi = 0; fi < 2; ++fi) IA::read(f.a[fi], slot + (2 * band + fi) * IA::kBytes, roff_a);
 #pragma unroll
-      for (int j = 0; j < NB; ++j) {
-        if (col[j] >= g.N) continue;
-        const float yc = epi<SYM>(acc[0][0][j][r] >> SHIFT, acc[NP - 1][0][j][r] >> SHIFT, sp, sn,
-                                  sw[j], g.inv_b);
-        const float yu = epi<SYM>(acc[0][1][j][r] >> SHIFT, acc[NP - 1][1][j][r] >> SHIFT, sp, sn,
-                                  sw[j], g.inv_b);
-        const float d = __fsub_rn(yc, yu);
-        const float tt = __fmul_rn(g.guidance, d);
-        yrow[col[j]] = __fadd_rn(yu, tt);
+    for (int jj = 0; jj < NBG; ++jj) {
+      const int j = min(j0 + jj, NB - 1);  // unused slot of group 1: harmless re-read
+      IW::read(f.w[jj], slot + Lay::kABytes + j * IW::kBytes, roff_w);
+    }
+  };
+
+  // DUAL: acc[0] = sum pos(c) w, acc[1] = sum c w (acc- = acc[1] - acc[0]).
+  v4i acc[NP][2][NBG];
+  auto zero_acc = [&]() {
+#pragma unroll
+    for (int p = 0; p < NP; ++p)
+#pragma unroll
+      for (int fi = 0; fi < 2; ++fi)
+#pragma unroll
+        for (int jj = 0; jj < NBG; ++jj) acc[p][fi][jj] = v4i{0, 0, 0, 0};
+  };
+
+  auto compute = [&](const Frags& f) {
+#pragma unroll
+    for (int fi = 0; fi < 2; ++fi) {
+      const v4i a = operand<A4>(f.a[fi]);
+      if constexpr (SYM) {
+#pragma unroll
+        for (int jj = 0; jj < NBG; ++jj)
+          if (jj < nbw) acc[0][fi][jj] = mfma(a, operand<W4>(f.w[jj]), acc[0][fi][jj]);
+      } else {
+        const v4i ap = positive(a);
+#pragma unroll
+        for (int jj = 0; jj < NBG; ++jj) {
+          if (jj < nbw) {
+            const v4i b = operand<W4>(f.w[jj]);
+            acc[0][fi][jj] = mfma(ap, b, acc[0][fi][jj]);
+            acc[1][fi][jj] = mfma(a, b, acc[1][fi][jj]);
+          }
+        }
       }
     }
-  } else {
+  };
+
+  // One K-step: wait for stage s+1 (this wave's DMA), barrier (stage s+1
+  // visible to all, slot of s-1 free), refill the ring with stage s+5,
+  // prefetch stage s+1's fragments, run stage s's MFMAs. u = s % kStages is
+  // a compile-time constant at every call site.
+  auto step = [&](int s, auto uc) {
+    constexpr int u = decltype(uc)::value;
+    if (s + kStages - 2 < total)
+      wait_stages(IC<kStages - 3>{});
+    else
+      wait_stages(IC<0>{});
+    __builtin_amdgcn_s_barrier();
+    if (s + kStages - 1 < total) issue(slots[(u + kStages - 1) % kStages]);
+    // (on the last step this reads a stale slot; the values are never used)
+    read_all(F[(u + 1) & 1], slots[(u + 1) % kStages]);
+    compute(F[u & 1]);
+  };
+
+  const float sp = g.act_scales[0];
+  const float sn = g.act_scales[1];
+  const int i16 = lane & 15;
+  const int rsub = (lane >> 4) * 4;
+
+  // (acc+, acc-) of accumulator slot (fi, jj, r), shifted back to code units.
+  auto accs = [&](int fi, int jj, int r, int& ap, int& an) {
+    ap = acc[0][fi][jj][r] >> SHIFT;
+    if constexpr (SYM)
+      an = 0;
+    else
+      an = (acc[NP - 1][fi][jj][r] - acc[0][fi][jj][r]) >> SHIFT;
+  };
+
+  auto epilogue = [&](int ti) {
+    int m0, n0;
+    coords(ti, m0, n0);
+    float sw[NBG];
+    int col[NBG];
 #pragma unroll
-    for (int fi = 0; fi < 2; ++fi)
+    for (int jj = 0; jj < NBG; ++jj) {
+      col[jj] = n0 + 16 * (j0 + jj) + i16;
+      sw[jj] = (jj < nbw && col[jj] < g.N) ? g.w_scales[col[jj]] : 0.0f;
+    }
+    if (g.dbg) {
+      const int64_t plane = (int64_t)g.M * g.N;
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        bool ok;
-        const int grow = grow_of(fi, rsub + r, ok);
-        if (!ok) continue;
-        float* yrow = g.Y + (int64_t)grow * g.N;
+      for (int fi = 0; fi < 2; ++fi)
 #pragma unroll
-        for (int j = 0; j < NB; ++j) {
-          if (col[j] >= g.N) continue;
-          yrow[col[j]] = epi<SYM>(acc[0][fi][j][r] >> SHIFT, acc[NP - 1][fi][j][r] >> SHIFT, sp,
-                                  sn, sw[j], g.inv_b);
+        for (int r = 0; r < 4; ++r) {
+          bool ok;
+          const int grow = a_row(m0, 2 * band + fi, rsub + r, ok);
+          if (!ok) continue;
+#pragma unroll
+          for (int jj = 0; jj < NBG; ++jj) {
+            if (jj >= nbw || col[jj] >= g.N) continue;
+            const int64_t e = (int64_t)grow * g.N + col[jj];
+            int ap, an;
+            accs(fi, jj, r, ap, an);
+            g.dbg[e] = ap;
+            g.dbg[plane + e] = an;
+          }
+        }
+    }
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      if constexpr (CFG) {
+        const int crow = m0 + 16 * band + rsub + r;
+        if (crow >= g.Mh) continue;
+        float* yrow = g.Y + (int64_t)crow * g.N;
+#pragma unroll
+        for (int jj = 0; jj < NBG; ++jj) {
+          if (jj >= nbw || col[jj] >= g.N) continue;
+          int cp, cn, up, un;
+          accs(0, jj, r, cp, cn);
+          accs(1, jj, r, up, un);
+          const float yc = epi<SYM>(cp, cn, sp, sn, sw[jj], g.inv_b);
+          const float yu = epi<SYM>(up, un, sp, sn, sw[jj], g.inv_b);
+          const float d = __fsub_rn(yc, yu);
+          const float t = __fmul_rn(g.guidance, d);
+          yrow[col[jj]] = __fadd_rn(yu, t);
+        }
+      } else {
+#pragma unroll
+        for (int fi = 0; fi < 2; ++fi) {
+          bool ok;
+          const int grow = a_row(m0, 2 * band + fi, rsub + r, ok);
+          if (!ok) continue;
+          float* yrow = g.Y + (int64_t)grow * g.N;
+#pragma unroll
+          for (int jj = 0; jj < NBG; ++jj) {
+            if (jj >= nbw || col[jj] >= g.N) continue;
+            int ap, an;
+            accs(fi, jj, r, ap, an);
+            yrow[col[jj]] = epi<SYM>(ap, an, sp, sn, sw[jj], g.inv_b);
+          }
         }
       }
+    }
+  };
+
+  // prologue: stages 0 .. 4 in flight, stage 0 landed
+  enter_tile(0);
+  issue(slots[0]);
+  if (1 < total) issue(slots[1]);
+  if (2 < total) issue(slots[2]);
+  if (3 < total) issue(slots[3]);
+  if (4 < total) issue(slots[4]);
+  if (total >= kStages - 1)
+    wait_stages(IC<kStages - 2>{});
+  else
+    wait_stages(IC<0>{});
+  __builtin_amdgcn_s_barrier();
+  read_all(F[0], slots[0]);
+
+  for (int ti = 0; ti < tl.count; ++ti) {
+    zero_acc();
+    const int s0 = ti * nkp;
+    for (int kb = 0; kb < nkp; kb += kStages) {
+      step(s0 + kb + 0, IC<0>{});
+      step(s0 + kb + 1, IC<1>{});
+      step(s0 + kb + 2, IC<2>{});
+      step(s0 + kb + 3, IC<3>{});
+      step(s0 + kb + 4, IC<4>{});
+      step(s0 + kb + 5, IC<5>{});
+    }
+    epilogue(ti);
   }
 }
 
+int g_cus = 0;  // compute units of the device (queried on first launch)
+
 template <bool A4, bool W4, bool SYM, bool CFG, int NB>
 hipError_t run(const GemmArgs& g, hipStream_t s) {
-  const int rows = CFG ? g.Mh : g.M;
-  const int rt = (rows + (CFG ? 63 : 127)) / (CFG ? 64 : 128);
-  const int ct = (g.N + 16 * NB - 1) / (16 * NB);
-  const dim3 grid(rt * ct);
-  if (g.dbg)
-    hipLaunchKernelGGL((k2_gemm<A4, W4, SYM, CFG, true, NB>), grid, dim3(kThreads), 0, s, g);
-  else
-    hipLaunchKernelGGL((k2_gemm<A4, W4, SYM, CFG, false, NB>), grid, dim3(kThreads), 0, s, g);
+  const int rpt = CFG ? 64 : 128;
+  const int T = (((CFG ? g.Mh : g.M) + rpt - 1) / rpt) * ((g.N + 16 * NB - 1) / (16 * NB));
+  if (g_cus <= 0) {
+    int dev = 0, cus = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+    if (e != hipSuccess) return e;
+    g_cus = cus;
+  }
+  const int G = T < g_cus ? T : g_cus;
+  hipLaunchKernelGGL((k2_gemm<A4, W4, SYM, CFG, NB>), dim3(G), dim3(kThreads), 0, s, g);
   return hipGetLastError();
 }
 

@@ -116,11 +116,21 @@ __device__ __forceinline__ int truncate_lsb(int c, int keep_mask) {
   return c < 0 ? -t : t;
 }
 
+// 0xFF in every byte of c that is negative as int8, 0x00 elsewhere.
+// v_perm_b32 selectors 8..11 replicate the sign bit of bytes 1, 3, 5, 7 of
+// the 64-bit pair {src0, src1}; with src0 = c and src1 = c << 8 those are the
+// sign bits of c's bytes 0, 2, 1, 3. Two full-rate instructions.
+__device__ __forceinline__ uint32_t neg_byte_mask(uint32_t c) {
+  return __builtin_amdgcn_perm(c, c << 8, 0x0B090A08u);
+}
+
+// Non-negative plane of four packed int8 codes (negative bytes zeroed).
+__device__ __forceinline__ uint32_t pos_plane(uint32_t c) { return c & ~neg_byte_mask(c); }
+
 // Polarity planes of four packed int8 codes: bytes < 0 go to `neg`, the
 // others to `pos` (the planes have disjoint support, so pos + neg = codes).
 __device__ __forceinline__ void split_polarity(uint32_t c, uint32_t& pos, uint32_t& neg) {
-  const uint32_t sign = (c >> 7) & 0x01010101u;
-  const uint32_t m = sign * 0xFFu;  // 0xFF in every negative byte
+  const uint32_t m = neg_byte_mask(c);
   pos = c & ~m;
   neg = c & m;
 }
