@@ -21,18 +21,16 @@
 //    column groups (w / 4) of ceil(NB/2) / floor(NB/2) fragments; the two
 //    waves sharing a SIMD carry NB fragments together.
 //  * Both operands go HBM -> LDS by buffer_load ... lds (no VGPR staging)
-//    into a ring of 6 K-steps, 5 steps ahead of the MFMAs; each fragment is
-//    loaded once per workgroup by one wave (17 loads per K-step for the
-//    whole workgroup). The DMA lanes read whole 64-byte row segments
-//    (coalesced) and the LDS image is XOR-swizzled so that the MFMA
-//    operand reads are bank-conflict free.
+//    into a ring of 4 steps of 128 K, 4 steps ahead of the MFMAs; each
+//    fragment pair is loaded once per workgroup by one wave. The DMA lanes
+//    read whole 128-byte lines (coalesced) and the LDS image is XOR-swizzled
+//    so that the MFMA operand reads are bank-conflict free.
 //  * Persistent workgroups: each one walks its tiles as one continuous
 //    stream of K-steps, so the loads of the next tile overlap the epilogue of
 //    the current one. Workgroups (whose id mod 8 is their XCD) get bands of
 //    consecutive tiles that share rows in that XCD's L2.
 //  * Every out-of-range row or K-chunk is read as zero by the buffer range
-//    check, so ragged M, N and K need no special path; K is padded to a
-//    multiple of 6 steps with such zero steps.
+//    check, so ragged M, N and K need no special path.
 //  * 4-bit codes stay packed through memory and LDS and are unpacked on the
 //    way into the MFMA, each code multiplied by 16 (nibble placed in the high
 //    half of its byte: two ANDs, a shift, two byte permutes); accumulators
@@ -58,8 +56,8 @@ using IC = std::integral_constant<int, V>;
 
 constexpr int kThreads = 512;
 constexpr int kWaves = 8;
-constexpr int BK = 64;                  // K elements per ring stage
-constexpr int kStages = 6;              // ring depth (= unroll of the K loop)
+constexpr int BK = 128;                 // K elements per ring stage
+constexpr int kStages = 4;              // ring depth (= unroll of the step loop)
 constexpr unsigned kOOB = 0x80000000u;  // offset beyond every buffer: loads return 0
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
@@ -74,17 +72,19 @@ __device__ __forceinline__ void wait_vmcnt() {
   __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
 }
 
-// LDS image of one 16-row x 64-K fragment and the DMA that fills it.
+// LDS image of a fragment pair (16 rows x 128 K, the two 16 x 64 MFMA
+// operands of one step) and the DMA that fills it.
 //
-// int8 (1 KB): one 16-byte DMA per lane. Lane p loads row p/4, chunk
-// (p%4) ^ ((p/16)%4) of the row's 64 bytes, so each group of 4 consecutive
-// lanes reads one contiguous 64-byte row segment (coalesced) and lane p's
-// bytes land at p*16. An MFMA lane l (row l%16, K-chunk l/16) then reads
-// position 4*(l%16) + ((l/16) ^ ((l%16)/4)): the 16 lanes that read together
-// hit 16 distinct 16-byte bank groups.
+// int8 (2 KB, two DMAs of 1 KB): DMA lane p of instruction i loads row
+// r = 8i + p/8, 16-byte chunk (p%8) ^ ((r/2)%8) of the row's 128 bytes, so
+// every 8 consecutive lanes read one whole 128-byte line (coalesced); lane
+// p's bytes land at i*1024 + p*16. MFMA lane l of half h (row l%16, chunk
+// 4h + l/16) finds its 16 bytes at the same swizzled position; the 16 lanes
+// read together hit 16 distinct 16-byte bank groups.
 //
-// packed 4-bit (512 B): two 4-byte DMAs per lane in MFMA order (lane l: row
-// l%16, bytes 8*(l/16) .. +8 of the row's 32), read back as two dwords.
+// packed 4-bit (1 KB, one DMA): DMA lane p loads row p/4, 16-byte chunk
+// (p%4) ^ ((p/16)%4) of the row's 64 bytes; MFMA lane l of half h reads the
+// 8 bytes of element group 4h + l/16 (8-byte half of one of those chunks).
 template <bool P4>
 struct Frag {
   uint32_t d[P4 ? 2 : 4];
@@ -92,42 +92,41 @@ struct Frag {
 
 template <bool P4>
 struct FragIO {
-  static constexpr int kBytes = P4 ? 512 : 1024;
-  static constexpr int kLoads = P4 ? 2 : 1;
-  // Row (0..15) inside the fragment that DMA lane p loads.
-  __device__ static __forceinline__ int dma_row(int p) { return P4 ? (p & 15) : (p >> 2); }
-  // K-chunk (16 elements) of the 64-element step that DMA lane p loads.
-  __device__ static __forceinline__ int dma_chunk(int p) {
-    return P4 ? (p >> 4) : ((p & 3) ^ ((p >> 4) & 3));
+  static constexpr int kBytes = P4 ? 1024 : 2048;  // fragment pair
+  static constexpr int kLoads = P4 ? 1 : 2;        // DMA instructions per pair
+  // Row (0..15) and 16-byte chunk that lane p of DMA instruction i loads.
+  __device__ static __forceinline__ int dma_row(int i, int p) {
+    return P4 ? (p >> 2) : (8 * i + (p >> 3));
   }
-  // Byte offset of that chunk inside a row's step.
-  __device__ static __forceinline__ unsigned chunk_off(int p) {
-    return (unsigned)dma_chunk(p) * (P4 ? 8u : 16u);
+  __device__ static __forceinline__ int dma_chunk(int i, int p) {
+    const int r = dma_row(i, p);
+    return P4 ? ((p & 3) ^ ((r >> 2) & 3)) : ((p & 7) ^ ((r >> 1) & 7));
   }
-  // Where MFMA lane l finds its operand inside the fragment.
-  __device__ static __forceinline__ int read_off(int l) {
-    if constexpr (P4) return l * 4;
+  // K elements covered by one 16-byte chunk.
+  static constexpr int kChunkElems = P4 ? 32 : 16;
+  // Where MFMA lane l finds half h of its operand pair inside the image.
+  __device__ static __forceinline__ int read_off(int l, int h) {
     const int r = l & 15;
-    return (4 * r + ((l >> 4) ^ (r >> 2))) * 16;
-  }
-  // DMA of this lane's part of the fragment into LDS at `dst` (wave-uniform).
-  __device__ static __forceinline__ void dma(__amdgpu_buffer_rsrc_t r, uint8_t* dst, unsigned voff,
-                                             unsigned soff) {
     if constexpr (P4) {
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)dst, 4, voff, soff, 0, 0);
-      // (+4 bytes through the scalar offset: an instruction offset would also
-      // move the LDS destination)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)(dst + 256), 4, voff, soff + 4u, 0, 0);
+      const int e = 4 * h + (l >> 4);  // 8-byte element group of the row
+      return (4 * r + ((e >> 1) ^ ((r >> 2) & 3))) * 16 + (e & 1) * 8;
     } else {
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)dst, 16, voff, soff, 0, 0);
+      const int c = 4 * h + (l >> 4);
+      return (r >> 3) * 1024 + (8 * (r & 7) + (c ^ ((r >> 1) & 7))) * 16;
     }
   }
-  __device__ static __forceinline__ void read(Frag<P4>& f, const uint8_t* frag, int roff) {
+  // One DMA instruction of the pair into LDS at `dst` (wave-uniform).
+  __device__ static __forceinline__ void dma(__amdgpu_buffer_rsrc_t r, uint8_t* dst, unsigned voff,
+                                             unsigned soff) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)dst, 16, voff, soff, 0, 0);
+  }
+  __device__ static __forceinline__ void read(Frag<P4>& f, const uint8_t* img, int roff) {
     if constexpr (P4) {
-      f.d[0] = *reinterpret_cast<const uint32_t*>(frag + roff);
-      f.d[1] = *reinterpret_cast<const uint32_t*>(frag + 256 + roff);
+      const uint2 v = *reinterpret_cast<const uint2*>(img + roff);
+      f.d[0] = v.x;
+      f.d[1] = v.y;
     } else {
-      const uint4 v = *reinterpret_cast<const uint4*>(frag + roff);
+      const uint4 v = *reinterpret_cast<const uint4*>(img + roff);
       f.d[0] = v.x;
       f.d[1] = v.y;
       f.d[2] = v.z;
@@ -140,11 +139,11 @@ template <bool A4, bool W4, int NB>
 struct Layout {
   static constexpr int kNB0 = (NB + 1) / 2;  // weight fragments of column group 0
   static constexpr int kNB1 = NB / 2;        // weight fragments of column group 1
-  static constexpr int kAFrags = 8;          // 128 rows
+  static constexpr int kAFrags = 8;          // 128 rows = 8 fragment pairs
   static constexpr int kABytes = kAFrags * FragIO<A4>::kBytes;
   static constexpr int kStage = kABytes + NB * FragIO<W4>::kBytes;
-  // DMA: wave w moves activation fragment w and weight fragment w, and waves
-  // w < NB - 8 also weight fragment w + 8.
+  // DMA: wave w moves activation pair w and weight pair w, and waves
+  // w < NB - 8 also weight pair w + 8.
   static_assert(NB >= 8 && NB <= 16, "fragment distribution");
   static constexpr int kOpsLow = FragIO<A4>::kLoads + 2 * FragIO<W4>::kLoads;  // waves < NB-8
   static constexpr int kOpsHigh = FragIO<A4>::kLoads + FragIO<W4>::kLoads;     // the others
@@ -219,6 +218,11 @@ __device__ __forceinline__ TileList my_tiles(int T) {
   return L;
 }
 
+// lgkmcnt-only wait (vmcnt / expcnt left at their maxima), gfx9 encoding.
+__device__ __forceinline__ void wait_lgkm0() {
+  __builtin_amdgcn_s_waitcnt(0xF | (0x3 << 14) | (0x7 << 4) | (0x0 << 8));
+}
+
 template <bool A4, bool W4, bool SYM, bool CFG, int NB>
 __global__ __launch_bounds__(kThreads, 1) void k2_gemm(GemmArgs g) {
   using Lay = Layout<A4, W4, NB>;
@@ -236,10 +240,8 @@ __global__ __launch_bounds__(kThreads, 1) void k2_gemm(GemmArgs g) {
   __shared__ __attribute__((aligned(16))) uint8_t st1[Lay::kStage];
   __shared__ __attribute__((aligned(16))) uint8_t st2[Lay::kStage];
   __shared__ __attribute__((aligned(16))) uint8_t st3[Lay::kStage];
-  __shared__ __attribute__((aligned(16))) uint8_t st4[Lay::kStage];
-  __shared__ __attribute__((aligned(16))) uint8_t st5[Lay::kStage];
-  static_assert(kStages == 6, "one LDS object per stage");
-  uint8_t* const slots[kStages] = {st0, st1, st2, st3, st4, st5};
+  static_assert(kStages == 4, "one LDS object per stage");
+  uint8_t* const slots[kStages] = {st0, st1, st2, st3};
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // uniform
@@ -247,7 +249,7 @@ __global__ __launch_bounds__(kThreads, 1) void k2_gemm(GemmArgs g) {
   const int cg = wave >> 2;           // column group
   const int j0 = cg ? Lay::kNB0 : 0;  // first weight fragment of this wave
   const int nbw = cg ? Lay::kNB1 : Lay::kNB0;
-  const bool two_w = wave < NB - 8;   // this wave also moves weight fragment w + 8
+  const bool two_w = wave < NB - 8;   // this wave also moves weight pair w + 8
 
   const int ct = (g.N + BN - 1) / BN;
   const int T = (((CFG ? g.Mh : g.M) + RPT - 1) / RPT) * ct;
@@ -255,23 +257,22 @@ __global__ __launch_bounds__(kThreads, 1) void k2_gemm(GemmArgs g) {
   if (tl.count == 0) return;
 
   const int nk = (g.K + BK - 1) / BK;
-  const int nkp = (nk + kStages - 1) / kStages * kStages;  // padded with zero steps
-  const int total = tl.count * nkp;
+  const int total = tl.count * nk;  // steps of this workgroup's stream
 
   const __amdgpu_buffer_rsrc_t ra = make_rsrc(g.A, (uint32_t)((int64_t)g.M * g.lda));
   const __amdgpu_buffer_rsrc_t rw = make_rsrc(g.W, (uint32_t)((int64_t)g.N * g.ldw));
 
-  auto coords = [&](int ti, int& m0, int& n0) {
+  auto coords = [&](int ti, int& m0, int& n0) __attribute__((always_inline)) {
     const int t = tl.at(ti);
     const int tr = t / ct;
     m0 = tr * RPT;
     n0 = (t - tr * ct) * BN;
   };
 
-  // Global row of row i (0..15) of activation fragment f (0..7) of a tile:
-  // fragment f belongs to row band f/2; with CFG, fragment 2b holds 16
-  // conditional rows and 2b+1 their unconditional partners.
-  auto a_row = [&](int m0, int f, int i, bool& ok) {
+  // Global row of row i (0..15) of activation pair f (0..7) of a tile: pair f
+  // belongs to row band f/2; with CFG, pair 2b holds 16 conditional rows and
+  // 2b+1 their unconditional partners.
+  auto a_row = [&](int m0, int f, int i, bool& ok) __attribute__((always_inline)) {
     if constexpr (CFG) {
       const int crow = m0 + 16 * (f >> 1) + i;
       ok = crow < g.Mh;
@@ -283,50 +284,61 @@ __global__ __launch_bounds__(kThreads, 1) void k2_gemm(GemmArgs g) {
     }
   };
 
-  // Load stream position (kStages-1 steps ahead of the MFMAs) and this lane's
-  // DMA row offsets for the stream's tile; the K offset of a step goes into
-  // the scalar operand of the loads.
+  // Load stream position (kStages steps ahead of the MFMAs) and this lane's
+  // DMA offsets for the stream's tile; the K offset of a step goes into the
+  // scalar operand of the loads.
   int iss_ti = 0, iss_k = 0;
-  unsigned av, wv0, wv1;
-  auto enter_tile = [&](int ti) {
+  unsigned av[IA::kLoads], wv[2][IW::kLoads];
+  auto enter_tile = [&](int ti) __attribute__((always_inline)) {
     int m0, n0;
     coords(ti, m0, n0);
-    bool ok;
-    const int r = a_row(m0, wave, IA::dma_row(lane), ok);
-    av = ok ? (unsigned)r * (unsigned)g.lda + IA::chunk_off(lane) : kOOB;
-    const int n_a = n0 + 16 * wave + IW::dma_row(lane);
-    wv0 = n_a < g.N ? (unsigned)n_a * (unsigned)g.ldw + IW::chunk_off(lane) : kOOB;
-    const int n_b = n0 + 16 * (wave + 8) + IW::dma_row(lane);
-    wv1 = n_b < g.N ? (unsigned)n_b * (unsigned)g.ldw + IW::chunk_off(lane) : kOOB;
+#pragma unroll
+    for (int i = 0; i < IA::kLoads; ++i) {
+      bool ok;
+      const int r = a_row(m0, wave, IA::dma_row(i, lane), ok);
+      av[i] = ok ? (unsigned)r * (unsigned)g.lda + 16u * (unsigned)IA::dma_chunk(i, lane) : kOOB;
+    }
+#pragma unroll
+    for (int q = 0; q < 2; ++q)
+#pragma unroll
+      for (int i = 0; i < IW::kLoads; ++i) {
+        const int n = n0 + 16 * (wave + 8 * q) + IW::dma_row(i, lane);
+        wv[q][i] = n < g.N ? (unsigned)n * (unsigned)g.ldw + 16u * (unsigned)IW::dma_chunk(i, lane)
+                           : kOOB;
+      }
   };
 
-  // Issue the stream's next stage into `slot`.
-  auto issue = [&](uint8_t* slot) {
+  // Issue the stream's next step into `slot`.
+  auto issue = [&](uint8_t* slot) __attribute__((always_inline)) {
     const int k0 = iss_k * BK;
-    unsigned a = av, w0 = wv0, w1 = wv1;
-    unsigned sa = (unsigned)k0 / (A4 ? 2u : 1u);
-    unsigned sw = (unsigned)k0 / (W4 ? 2u : 1u);
-    if (k0 >= g.K) {
-      sa = kOOB;  // padding step: zeros
-      sw = kOOB;
-    } else if (k0 + BK > g.K) {
-      // ragged last step: chunks past K read zeros
-      a = k0 + 16 * IA::dma_chunk(lane) < g.K ? a : kOOB;
-      const bool win = k0 + 16 * IW::dma_chunk(lane) < g.K;
-      w0 = win ? w0 : kOOB;
-      w1 = win ? w1 : kOOB;
+    const unsigned sa = (unsigned)k0 / (A4 ? 2u : 1u);
+    const unsigned sw = (unsigned)k0 / (W4 ? 2u : 1u);
+    const bool ragged = k0 + BK > g.K;  // chunks past K must read zeros
+#pragma unroll
+    for (int i = 0; i < IA::kLoads; ++i) {
+      unsigned v = av[i];
+      if (ragged && k0 + IA::kChunkElems * IA::dma_chunk(i, lane) >= g.K) v = kOOB;
+      IA::dma(ra, slot + wave * IA::kBytes + i * 1024, v, sa);
     }
-    IA::dma(ra, slot + wave * IA::kBytes, a, sa);
-    IW::dma(rw, slot + Lay::kABytes + wave * IW::kBytes, w0, sw);
-    if (two_w) IW::dma(rw, slot + Lay::kABytes + (wave + 8) * IW::kBytes, w1, sw);
-    if (++iss_k == nkp) {
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+      if (q == 0 || two_w) {
+#pragma unroll
+        for (int i = 0; i < IW::kLoads; ++i) {
+          unsigned v = wv[q][i];
+          if (ragged && k0 + IW::kChunkElems * IW::dma_chunk(i, lane) >= g.K) v = kOOB;
+          IW::dma(rw, slot + Lay::kABytes + (wave + 8 * q) * IW::kBytes + i * 1024, v, sw);
+        }
+      }
+    }
+    if (++iss_k == nk) {
       iss_k = 0;
       if (++iss_ti < tl.count) enter_tile(iss_ti);
     }
   };
 
-  // Wait until at most N of this wave's stages are in flight (its own DMA).
-  auto wait_stages = [&](auto nc) {
+  // Wait until at most n of this wave's issued steps are still in flight.
+  auto wait_steps = [&](auto nc) __attribute__((always_inline)) {
     constexpr int n = decltype(nc)::value;
     if (two_w)
       wait_vmcnt<n * Lay::kOpsLow>();
@@ -334,27 +346,35 @@ __global__ __launch_bounds__(kThreads, 1) void k2_gemm(GemmArgs g) {
       wait_vmcnt<n * Lay::kOpsHigh>();
   };
 
-  const int roff_a = IA::read_off(lane);
-  const int roff_w = IW::read_off(lane);
+  int roff_a[2], roff_w[2];
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    roff_a[h] = IA::read_off(lane, h);
+    roff_w[h] = IW::read_off(lane, h);
+  }
 
   struct Frags {
-    Frag<A4> a[2];
-    Frag<W4> w[NBG];
+    Frag<A4> a[2][2];    // [pair of the band][half]
+    Frag<W4> w[NBG][2];  // [fragment slot][half]
   };
   Frags F[2];
-  auto read_all = [&](Frags& f, const uint8_t* slot) {
+  auto read_all = [&](Frags& f, const uint8_t* slot) __attribute__((always_inline)) {
 #pragma unroll
-    for (int fi = 0; fi < 2; ++fi) IA::read(f.a[fi], slot + (2 * band + fi) * IA::kBytes, roff_a);
+    for (int h = 0; h < 2; ++h) {
 #pragma unroll
-    for (int jj = 0; jj < NBG; ++jj) {
-      const int j = min(j0 + jj, NB - 1);  // unused slot of group 1: harmless re-read
-      IW::read(f.w[jj], slot + Lay::kABytes + j * IW::kBytes, roff_w);
+      for (int fi = 0; fi < 2; ++fi)
+        IA::read(f.a[fi][h], slot + (2 * band + fi) * IA::kBytes, roff_a[h]);
+#pragma unroll
+      for (int jj = 0; jj < NBG; ++jj) {
+        const int j = min(j0 + jj, NB - 1);  // unused slot of group 1: harmless re-read
+        IW::read(f.w[jj][h], slot + Lay::kABytes + j * IW::kBytes, roff_w[h]);
+      }
     }
   };
 
   // DUAL: acc[0] = sum pos(c) w, acc[1] = sum c w (acc- = acc[1] - acc[0]).
   v4i acc[NP][2][NBG];
-  auto zero_acc = [&]() {
+  auto zero_acc = [&]() __attribute__((always_inline)) {
 #pragma unroll
     for (int p = 0; p < NP; ++p)
 #pragma unroll
@@ -363,43 +383,28 @@ __global__ __launch_bounds__(kThreads, 1) void k2_gemm(GemmArgs g) {
         for (int jj = 0; jj < NBG; ++jj) acc[p][fi][jj] = v4i{0, 0, 0, 0};
   };
 
-  auto compute = [&](const Frags& f) {
+  auto compute = [&](const Frags& f) __attribute__((always_inline)) {
 #pragma unroll
-    for (int fi = 0; fi < 2; ++fi) {
-      const v4i a = operand<A4>(f.a[fi]);
-      if constexpr (SYM) {
+    for (int h = 0; h < 2; ++h)
 #pragma unroll
-        for (int jj = 0; jj < NBG; ++jj)
-          if (jj < nbw) acc[0][fi][jj] = mfma(a, operand<W4>(f.w[jj]), acc[0][fi][jj]);
-      } else {
-        const v4i ap = positive(a);
+      for (int fi = 0; fi < 2; ++fi) {
+        const v4i a = operand<A4>(f.a[fi][h]);
+        if constexpr (SYM) {
 #pragma unroll
-        for (int jj = 0; jj < NBG; ++jj) {
-          if (jj < nbw) {
-            const v4i b = operand<W4>(f.w[jj]);
-            acc[0][fi][jj] = mfma(ap, b, acc[0][fi][jj]);
-            acc[1][fi][jj] = mfma(a, b, acc[1][fi][jj]);
+          for (int jj = 0; jj < NBG; ++jj)
+            if (jj < nbw) acc[0][fi][jj] = mfma(a, operand<W4>(f.w[jj][h]), acc[0][fi][jj]);
+        } else {
+          const v4i ap = positive(a);
+#pragma unroll
+          for (int jj = 0; jj < NBG; ++jj) {
+            if (jj < nbw) {
+              const v4i b = operand<W4>(f.w[jj][h]);
+              acc[0][fi][jj] = mfma(ap, b, acc[0][fi][jj]);
+              acc[1][fi][jj] = mfma(a, b, acc[1][fi][jj]);
+            }
           }
         }
       }
-    }
-  };
-
-  // One K-step: wait for stage s+1 (this wave's DMA), barrier (stage s+1
-  // visible to all, slot of s-1 free), refill the ring with stage s+5,
-  // prefetch stage s+1's fragments, run stage s's MFMAs. u = s % kStages is
-  // a compile-time constant at every call site.
-  auto step = [&](int s, auto uc) {
-    constexpr int u = decltype(uc)::value;
-    if (s + kStages - 2 < total)
-      wait_stages(IC<kStages - 3>{});
-    else
-      wait_stages(IC<0>{});
-    __builtin_amdgcn_s_barrier();
-    if (s + kStages - 1 < total) issue(slots[(u + kStages - 1) % kStages]);
-    // (on the last step this reads a stale slot; the values are never used)
-    read_all(F[(u + 1) & 1], slots[(u + 1) % kStages]);
-    compute(F[u & 1]);
   };
 
   const float sp = g.act_scales[0];
@@ -408,7 +413,7 @@ __global__ __launch_bounds__(kThreads, 1) void k2_gemm(GemmArgs g) {
   const int rsub = (lane >> 4) * 4;
 
   // (acc+, acc-) of accumulator slot (fi, jj, r), shifted back to code units.
-  auto accs = [&](int fi, int jj, int r, int& ap, int& an) {
+  auto accs = [&](int fi, int jj, int r, int& ap, int& an) __attribute__((always_inline)) {
     ap = acc[0][fi][jj][r] >> SHIFT;
     if constexpr (SYM)
       an = 0;
@@ -416,7 +421,7 @@ __global__ __launch_bounds__(kThreads, 1) void k2_gemm(GemmArgs g) {
       an = (acc[NP - 1][fi][jj][r] - acc[0][fi][jj][r]) >> SHIFT;
   };
 
-  auto epilogue = [&](int ti) {
+  auto epilogue = [&](int ti) __attribute__((always_inline)) {
     int m0, n0;
     coords(ti, m0, n0);
     float sw[NBG];
@@ -483,33 +488,59 @@ __global__ __launch_bounds__(kThreads, 1) void k2_gemm(GemmArgs g) {
     }
   };
 
-  // prologue: stages 0 .. 4 in flight, stage 0 landed
+  int cmp_ti = 0, cmp_k = 0;  // compute position
+
+  // One step: wait for step s+1 (this wave's DMA) and for this wave's reads
+  // of step s (so its slot is free), barrier (step s+1 visible to all, slot
+  // of step s free everywhere), refill that slot with step s+4, read step
+  // s+1's fragments, run step s's MFMAs, and write the tile out when it ends.
+  // u = s % kStages is a compile-time constant at every call site.
+  auto step = [&](int s, auto uc) __attribute__((always_inline)) {
+    constexpr int u = decltype(uc)::value;
+    if (s + 3 < total)
+      wait_steps(IC<2>{});
+    else if (s + 2 < total)
+      wait_steps(IC<1>{});
+    else
+      wait_steps(IC<0>{});
+    wait_lgkm0();
+    __builtin_amdgcn_s_barrier();
+    if (s + kStages < total) issue(slots[u]);
+    // (on the last step this reads a stale slot; the values are never used)
+    read_all(F[(u + 1) & 1], slots[(u + 1) % kStages]);
+    compute(F[u & 1]);
+    if (++cmp_k == nk) {
+      epilogue(cmp_ti);
+      zero_acc();
+      cmp_k = 0;
+      ++cmp_ti;
+    }
+  };
+
+  // prologue: steps 0 .. 3 in flight, step 0 landed and read
   enter_tile(0);
   issue(slots[0]);
   if (1 < total) issue(slots[1]);
   if (2 < total) issue(slots[2]);
   if (3 < total) issue(slots[3]);
-  if (4 < total) issue(slots[4]);
-  if (total >= kStages - 1)
-    wait_stages(IC<kStages - 2>{});
+  if (total >= 4)
+    wait_steps(IC<3>{});
   else
-    wait_stages(IC<0>{});
+    wait_steps(IC<0>{});
   __builtin_amdgcn_s_barrier();
   read_all(F[0], slots[0]);
+  zero_acc();
 
-  for (int ti = 0; ti < tl.count; ++ti) {
-    zero_acc();
-    const int s0 = ti * nkp;
-    for (int kb = 0; kb < nkp; kb += kStages) {
-      step(s0 + kb + 0, IC<0>{});
-      step(s0 + kb + 1, IC<1>{});
-      step(s0 + kb + 2, IC<2>{});
-      step(s0 + kb + 3, IC<3>{});
-      step(s0 + kb + 4, IC<4>{});
-      step(s0 + kb + 5, IC<5>{});
-    }
-    epilogue(ti);
+  int sb = 0;
+  for (; sb + kStages <= total; sb += kStages) {
+    step(sb + 0, IC<0>{});
+    step(sb + 1, IC<1>{});
+    step(sb + 2, IC<2>{});
+    step(sb + 3, IC<3>{});
   }
+  if (sb + 0 < total) step(sb + 0, IC<0>{});
+  if (sb + 1 < total) step(sb + 1, IC<1>{});
+  if (sb + 2 < total) step(sb + 2, IC<2>{});
 }
 
 int g_cus = 0;  // compute units of the device (queried on first launch)
