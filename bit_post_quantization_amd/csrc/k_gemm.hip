@@ -55,7 +55,6 @@ template <int V>
 using IC = std::integral_constant<int, V>;
 
 constexpr int kThreads = 512;
-constexpr int kWaves = 8;
 constexpr int BK = 128;                 // K elements per ring stage
 constexpr int kStages = 4;              // ring depth (= unroll of the step loop)
 constexpr unsigned kOOB = 0x80000000u;  // offset beyond every buffer: loads return 0
@@ -223,33 +222,74 @@ __device__ __forceinline__ void wait_lgkm0() {
   __builtin_amdgcn_s_waitcnt(0xF | (0x3 << 14) | (0x7 << 4) | (0x0 << 8));
 }
 
-template <bool A4, bool W4, bool SYM, bool CFG, int NB>
-__global__ __launch_bounds__(kThreads, 1) void k2_gemm(GemmArgs g) {
+// Instruction-mix masks of __builtin_amdgcn_sched_group_barrier.
+constexpr int kSchedValu = 0x002;
+constexpr int kSchedMfma = 0x008;
+constexpr int kSchedDsRead = 0x100;
+
+// Issue order of one step's straight-line body: the activation-fragment
+// groups (half h, pair fi) each run their NBW MFMAs on the full codes, with
+// the polarity split / unpack VALU work of that group slotted between them,
+// then the NBW MFMAs on the non-negative plane with the next step's LDS
+// reads slotted between them. MFMAs never wait behind a burst of reads or
+// VALU work, and the LDS traffic spreads over the whole step.
+template <int MASK, int COUNT>
+__device__ __forceinline__ void sched_group() {
+  if constexpr (COUNT > 0) __builtin_amdgcn_sched_group_barrier(MASK, COUNT, 0);
+}
+
+// NBW MFMAs, each followed by VPER VALU instructions and, for the first NR of
+// them, one LDS read.
+template <int JJ, int NBW, int VPER, int NR>
+__device__ __forceinline__ void sched_mfmas() {
+  if constexpr (JJ < NBW) {
+    sched_group<kSchedMfma, 1>();
+    sched_group<kSchedValu, VPER>();
+    sched_group<kSchedDsRead, (JJ < NR ? 1 : 0)>();
+    sched_mfmas<JJ + 1, NBW, VPER, NR>();
+  }
+}
+
+template <int GR, int NBW, int NREADS, int VPER, bool DUAL>
+__device__ __forceinline__ void sched_groups() {
+  if constexpr (GR < 4) {
+    constexpr int nr = NREADS * (GR + 1) / 4 - NREADS * GR / 4;
+    if constexpr (DUAL) {
+      sched_mfmas<0, NBW, VPER, 0>();
+      sched_mfmas<0, NBW, 0, nr>();
+    } else {
+      sched_mfmas<0, NBW, VPER, nr>();
+    }
+    sched_group<kSchedDsRead, (nr > NBW ? nr - NBW : 0)>();
+    sched_groups<GR + 1, NBW, NREADS, VPER, DUAL>();
+  }
+}
+
+template <int NBW, int NREADS, int VALU_PER_GROUP, bool DUAL>
+__device__ __forceinline__ void schedule_step() {
+  sched_groups<0, NBW, NREADS, (VALU_PER_GROUP + NBW - 1) / NBW, DUAL>();
+}
+
+// The work of one wave. CG (column group) fixes at compile time how many
+// weight fragments the wave multiplies and TW whether it also moves weight
+// pair w + 8, so a step's body has no branches and every step issues the
+// same number of loads: the compiler can then prove from the explicit
+// waits below that each LDS read finds its data landed.
+template <bool A4, bool W4, bool SYM, bool CFG, int NB, int CG, bool TW>
+__device__ __forceinline__ void gemm_wave(const GemmArgs& g, int wave, int lane, uint8_t* st0,
+                                          uint8_t* st1, uint8_t* st2, uint8_t* st3) {
   using Lay = Layout<A4, W4, NB>;
   using IA = FragIO<A4>;
   using IW = FragIO<W4>;
   constexpr int NP = SYM ? 1 : 2;                     // accumulator planes
   constexpr int SHIFT = (A4 ? 4 : 0) + (W4 ? 4 : 0);  // undo the x16 unpack
   constexpr int BN = 16 * NB;
-  constexpr int NBG = Lay::kNB0;                      // weight fragment slots per wave
+  constexpr int NBW = CG ? Lay::kNB1 : Lay::kNB0;     // weight fragments of this wave
+  constexpr int J0 = CG ? Lay::kNB0 : 0;              // first weight fragment of this wave
   constexpr int RPT = CFG ? 64 : 128;                 // output rows per tile
-
-  // One LDS object per ring stage: the compiler tracks DMA -> LDS writes per
-  // object, so a fragment read waits only for the DMA of its own stage.
-  __shared__ __attribute__((aligned(16))) uint8_t st0[Lay::kStage];
-  __shared__ __attribute__((aligned(16))) uint8_t st1[Lay::kStage];
-  __shared__ __attribute__((aligned(16))) uint8_t st2[Lay::kStage];
-  __shared__ __attribute__((aligned(16))) uint8_t st3[Lay::kStage];
-  static_assert(kStages == 4, "one LDS object per stage");
   uint8_t* const slots[kStages] = {st0, st1, st2, st3};
 
-  const int lane = threadIdx.x & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // uniform
-  const int band = wave & 3;          // row band: 32 rows of the tile
-  const int cg = wave >> 2;           // column group
-  const int j0 = cg ? Lay::kNB0 : 0;  // first weight fragment of this wave
-  const int nbw = cg ? Lay::kNB1 : Lay::kNB0;
-  const bool two_w = wave < NB - 8;   // this wave also moves weight pair w + 8
+  const int band = wave & 3;  // row band: 32 rows of the tile
 
   const int ct = (g.N + BN - 1) / BN;
   const int T = (((CFG ? g.Mh : g.M) + RPT - 1) / RPT) * ct;
@@ -308,7 +348,9 @@ __global__ __launch_bounds__(kThreads, 1) void k2_gemm(GemmArgs g) {
       }
   };
 
-  // Issue the stream's next step into `slot`.
+  // Issue the stream's next step into `slot`. Past the end of the stream
+  // the same loads are issued with out-of-range offsets (they write zeros
+  // into slots nothing reads), so every step issues the same loads.
   auto issue = [&](uint8_t* slot) __attribute__((always_inline)) {
     const int k0 = iss_k * BK;
     const unsigned sa = (unsigned)k0 / (A4 ? 2u : 1u);
@@ -322,7 +364,7 @@ __global__ __launch_bounds__(kThreads, 1) void k2_gemm(GemmArgs g) {
     }
 #pragma unroll
     for (int q = 0; q < 2; ++q) {
-      if (q == 0 || two_w) {
+      if (q == 0 || TW) {
 #pragma unroll
         for (int i = 0; i < IW::kLoads; ++i) {
           unsigned v = wv[q][i];
@@ -333,17 +375,23 @@ __global__ __launch_bounds__(kThreads, 1) void k2_gemm(GemmArgs g) {
     }
     if (++iss_k == nk) {
       iss_k = 0;
-      if (++iss_ti < tl.count) enter_tile(iss_ti);
+      if (++iss_ti < tl.count) {
+        enter_tile(iss_ti);
+      } else {
+#pragma unroll
+        for (int i = 0; i < IA::kLoads; ++i) av[i] = kOOB;
+#pragma unroll
+        for (int q = 0; q < 2; ++q)
+#pragma unroll
+          for (int i = 0; i < IW::kLoads; ++i) wv[q][i] = kOOB;
+      }
     }
   };
 
   // Wait until at most n of this wave's issued steps are still in flight.
   auto wait_steps = [&](auto nc) __attribute__((always_inline)) {
     constexpr int n = decltype(nc)::value;
-    if (two_w)
-      wait_vmcnt<n * Lay::kOpsLow>();
-    else
-      wait_vmcnt<n * Lay::kOpsHigh>();
+    wait_vmcnt<n * (TW ? Lay::kOpsLow : Lay::kOpsHigh)>();
   };
 
   int roff_a[2], roff_w[2];
@@ -355,7 +403,7 @@ __global__ __launch_bounds__(kThreads, 1) void k2_gemm(GemmArgs g) {
 
   struct Frags {
     Frag<A4> a[2][2];    // [pair of the band][half]
-    Frag<W4> w[NBG][2];  // [fragment slot][half]
+    Frag<W4> w[NBW][2];  // [fragment slot][half]
   };
   Frags F[2];
   auto read_all = [&](Frags& f, const uint8_t* slot) __attribute__((always_inline)) {
@@ -365,46 +413,47 @@ __global__ __launch_bounds__(kThreads, 1) void k2_gemm(GemmArgs g) {
       for (int fi = 0; fi < 2; ++fi)
         IA::read(f.a[fi][h], slot + (2 * band + fi) * IA::kBytes, roff_a[h]);
 #pragma unroll
-      for (int jj = 0; jj < NBG; ++jj) {
-        const int j = min(j0 + jj, NB - 1);  // unused slot of group 1: harmless re-read
-        IW::read(f.w[jj][h], slot + Lay::kABytes + j * IW::kBytes, roff_w[h]);
-      }
+      for (int jj = 0; jj < NBW; ++jj)
+        IW::read(f.w[jj][h], slot + Lay::kABytes + (J0 + jj) * IW::kBytes, roff_w[h]);
     }
   };
 
   // DUAL: acc[0] = sum pos(c) w, acc[1] = sum c w (acc- = acc[1] - acc[0]).
-  v4i acc[NP][2][NBG];
+  v4i acc[NP][2][NBW];
   auto zero_acc = [&]() __attribute__((always_inline)) {
 #pragma unroll
     for (int p = 0; p < NP; ++p)
 #pragma unroll
       for (int fi = 0; fi < 2; ++fi)
 #pragma unroll
-        for (int jj = 0; jj < NBG; ++jj) acc[p][fi][jj] = v4i{0, 0, 0, 0};
+        for (int jj = 0; jj < NBW; ++jj) acc[p][fi][jj] = v4i{0, 0, 0, 0};
   };
 
-  auto compute = [&](const Frags& f) __attribute__((always_inline)) {
+  // Step s's MFMAs on `f` plus the reads of step s+1's fragments into `n`,
+  // issued in the interleaved order of schedule_step.
+  auto compute = [&](const Frags& f, Frags& n, const uint8_t* nslot) __attribute__((always_inline)) {
+    read_all(n, nslot);
+    v4i b[NBW][2];
+#pragma unroll
+    for (int jj = 0; jj < NBW; ++jj)
+#pragma unroll
+      for (int h = 0; h < 2; ++h) b[jj][h] = operand<W4>(f.w[jj][h]);
 #pragma unroll
     for (int h = 0; h < 2; ++h)
 #pragma unroll
       for (int fi = 0; fi < 2; ++fi) {
         const v4i a = operand<A4>(f.a[fi][h]);
-        if constexpr (SYM) {
 #pragma unroll
-          for (int jj = 0; jj < NBG; ++jj)
-            if (jj < nbw) acc[0][fi][jj] = mfma(a, operand<W4>(f.w[jj][h]), acc[0][fi][jj]);
-        } else {
+        for (int jj = 0; jj < NBW; ++jj) acc[NP - 1][fi][jj] = mfma(a, b[jj][h], acc[NP - 1][fi][jj]);
+        if constexpr (!SYM) {
           const v4i ap = positive(a);
 #pragma unroll
-          for (int jj = 0; jj < NBG; ++jj) {
-            if (jj < nbw) {
-              const v4i b = operand<W4>(f.w[jj][h]);
-              acc[0][fi][jj] = mfma(ap, b, acc[0][fi][jj]);
-              acc[1][fi][jj] = mfma(a, b, acc[1][fi][jj]);
-            }
-          }
+          for (int jj = 0; jj < NBW; ++jj) acc[0][fi][jj] = mfma(ap, b[jj][h], acc[0][fi][jj]);
         }
       }
+    constexpr int kReads = 4 + 2 * NBW;
+    constexpr int kValu = (SYM ? 0 : 12) + (A4 ? 10 : 0) + (W4 ? (10 * NBW + 1) / 2 : 0);
+    schedule_step<NBW, kReads, kValu, !SYM>();
   };
 
   const float sp = g.act_scales[0];
@@ -421,17 +470,60 @@ __global__ __launch_bounds__(kThreads, 1) void k2_gemm(GemmArgs g) {
       an = (acc[NP - 1][fi][jj][r] - acc[0][fi][jj][r]) >> SHIFT;
   };
 
+  // Tile epilogue. The scales of the tile's columns are loaded first and
+  // waited for once; the outputs then go out through range-checked buffer
+  // stores (rows past the end and columns past N are dropped by the range
+  // check), so no store waits on another and there are no per-element
+  // branches.
   auto epilogue = [&](int ti) __attribute__((always_inline)) {
     int m0, n0;
     coords(ti, m0, n0);
-    float sw[NBG];
-    int col[NBG];
+    float sw[NBW];
+    unsigned coff[NBW];  // byte offset of this lane's column in a row, or out of range
 #pragma unroll
-    for (int jj = 0; jj < NBG; ++jj) {
-      col[jj] = n0 + 16 * (j0 + jj) + i16;
-      sw[jj] = (jj < nbw && col[jj] < g.N) ? g.w_scales[col[jj]] : 0.0f;
+    for (int jj = 0; jj < NBW; ++jj) {
+      const int col = n0 + 16 * (J0 + jj) + i16;
+      sw[jj] = g.w_scales[min(col, g.N - 1)];
+      coff[jj] = col < g.N ? 4u * (unsigned)col : kOOB;
     }
-    if (g.dbg) {
+#pragma unroll
+    for (int jj = 0; jj < NBW; ++jj) asm volatile("" ::"v"(sw[jj]));
+    const int rows_here = min(RPT, (CFG ? g.Mh : g.M) - m0);
+    const __amdgpu_buffer_rsrc_t ry =
+        make_rsrc(g.Y + (int64_t)m0 * g.N, (uint32_t)rows_here * (uint32_t)g.N * 4u);
+    const unsigned rowb = (unsigned)g.N * 4u;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      if constexpr (CFG) {
+        const unsigned ro = (unsigned)(16 * band + rsub + r) * rowb;
+#pragma unroll
+        for (int jj = 0; jj < NBW; ++jj) {
+          int cp, cn, up, un;
+          accs(0, jj, r, cp, cn);
+          accs(1, jj, r, up, un);
+          const float yc = epi<SYM>(cp, cn, sp, sn, sw[jj], g.inv_b);
+          const float yu = epi<SYM>(up, un, sp, sn, sw[jj], g.inv_b);
+          const float d = __fsub_rn(yc, yu);
+          const float t = __fmul_rn(g.guidance, d);
+          __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(__fadd_rn(yu, t)), ry,
+                                                ro + coff[jj], 0, 0);
+        }
+      } else {
+#pragma unroll
+        for (int fi = 0; fi < 2; ++fi) {
+          const unsigned ro = (unsigned)(16 * (2 * band + fi) + rsub + r) * rowb;
+#pragma unroll
+          for (int jj = 0; jj < NBW; ++jj) {
+            int ap, an;
+            accs(fi, jj, r, ap, an);
+            __builtin_amdgcn_raw_buffer_store_b32(
+                __float_as_uint(epi<SYM>(ap, an, sp, sn, sw[jj], g.inv_b)), ry, ro + coff[jj],
+                0, 0);
+          }
+        }
+      }
+    }
+    if (g.dbg) {  // accumulator dump (testing aid)
       const int64_t plane = (int64_t)g.M * g.N;
 #pragma unroll
       for (int fi = 0; fi < 2; ++fi)
@@ -441,9 +533,9 @@ __global__ __launch_bounds__(kThreads, 1) void k2_gemm(GemmArgs g) {
           const int grow = a_row(m0, 2 * band + fi, rsub + r, ok);
           if (!ok) continue;
 #pragma unroll
-          for (int jj = 0; jj < NBG; ++jj) {
-            if (jj >= nbw || col[jj] >= g.N) continue;
-            const int64_t e = (int64_t)grow * g.N + col[jj];
+          for (int jj = 0; jj < NBW; ++jj) {
+            if (coff[jj] == kOOB) continue;
+            const int64_t e = (int64_t)grow * g.N + (coff[jj] >> 2);
             int ap, an;
             accs(fi, jj, r, ap, an);
             g.dbg[e] = ap;
@@ -451,96 +543,84 @@ __global__ __launch_bounds__(kThreads, 1) void k2_gemm(GemmArgs g) {
           }
         }
     }
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      if constexpr (CFG) {
-        const int crow = m0 + 16 * band + rsub + r;
-        if (crow >= g.Mh) continue;
-        float* yrow = g.Y + (int64_t)crow * g.N;
-#pragma unroll
-        for (int jj = 0; jj < NBG; ++jj) {
-          if (jj >= nbw || col[jj] >= g.N) continue;
-          int cp, cn, up, un;
-          accs(0, jj, r, cp, cn);
-          accs(1, jj, r, up, un);
-          const float yc = epi<SYM>(cp, cn, sp, sn, sw[jj], g.inv_b);
-          const float yu = epi<SYM>(up, un, sp, sn, sw[jj], g.inv_b);
-          const float d = __fsub_rn(yc, yu);
-          const float t = __fmul_rn(g.guidance, d);
-          yrow[col[jj]] = __fadd_rn(yu, t);
-        }
-      } else {
-#pragma unroll
-        for (int fi = 0; fi < 2; ++fi) {
-          bool ok;
-          const int grow = a_row(m0, 2 * band + fi, rsub + r, ok);
-          if (!ok) continue;
-          float* yrow = g.Y + (int64_t)grow * g.N;
-#pragma unroll
-          for (int jj = 0; jj < NBG; ++jj) {
-            if (jj >= nbw || col[jj] >= g.N) continue;
-            int ap, an;
-            accs(fi, jj, r, ap, an);
-            yrow[col[jj]] = epi<SYM>(ap, an, sp, sn, sw[jj], g.inv_b);
-          }
-        }
-      }
-    }
+    // Let the stores complete here, while no load is in flight: pending
+    // stores would otherwise leave the compiler unable to account the loads
+    // of the next steps, and it would drain the whole load stream later.
+    wait_vmcnt<0>();
   };
 
   int cmp_ti = 0, cmp_k = 0;  // compute position
 
   // One step: wait for step s+1 (this wave's DMA) and for this wave's reads
   // of step s (so its slot is free), barrier (step s+1 visible to all, slot
-  // of step s free everywhere), refill that slot with step s+4, read step
-  // s+1's fragments, run step s's MFMAs, and write the tile out when it ends.
-  // u = s % kStages is a compile-time constant at every call site.
+  // of step s free everywhere), refill that slot with step s+4, then run
+  // step s's MFMAs interleaved with the reads of step s+1's fragments.
+  // Returns true when step s ends a tile. u = s % kStages is a compile-time
+  // constant at every call site.
   auto step = [&](int s, auto uc) __attribute__((always_inline)) {
     constexpr int u = decltype(uc)::value;
-    if (s + 3 < total)
-      wait_steps(IC<2>{});
-    else if (s + 2 < total)
-      wait_steps(IC<1>{});
-    else
-      wait_steps(IC<0>{});
+    wait_steps(IC<2>{});
     wait_lgkm0();
     __builtin_amdgcn_s_barrier();
-    if (s + kStages < total) issue(slots[u]);
+    issue(slots[u]);
     // (on the last step this reads a stale slot; the values are never used)
-    read_all(F[(u + 1) & 1], slots[(u + 1) % kStages]);
-    compute(F[u & 1]);
-    if (++cmp_k == nk) {
+    compute(F[u & 1], F[(u + 1) & 1], slots[(u + 1) % kStages]);
+    return ++cmp_k == nk;
+  };
+
+  // prologue: steps 0 .. 3 in flight, step 0 landed and read
+  enter_tile(0);
+  issue(slots[0]);
+  issue(slots[1]);
+  issue(slots[2]);
+  issue(slots[3]);
+  wait_steps(IC<3>{});
+  __builtin_amdgcn_s_barrier();
+  read_all(F[0], slots[0]);
+  zero_acc();
+
+  // The ring cycle is unrolled by its depth so that slots and fragment
+  // buffers are static.
+  auto step_epi = [&](int s, auto uc) __attribute__((always_inline)) {
+    if (step(s, uc)) {
       epilogue(cmp_ti);
       zero_acc();
       cmp_k = 0;
       ++cmp_ti;
     }
   };
-
-  // prologue: steps 0 .. 3 in flight, step 0 landed and read
-  enter_tile(0);
-  issue(slots[0]);
-  if (1 < total) issue(slots[1]);
-  if (2 < total) issue(slots[2]);
-  if (3 < total) issue(slots[3]);
-  if (total >= 4)
-    wait_steps(IC<3>{});
-  else
-    wait_steps(IC<0>{});
-  __builtin_amdgcn_s_barrier();
-  read_all(F[0], slots[0]);
-  zero_acc();
-
   int sb = 0;
   for (; sb + kStages <= total; sb += kStages) {
-    step(sb + 0, IC<0>{});
-    step(sb + 1, IC<1>{});
-    step(sb + 2, IC<2>{});
-    step(sb + 3, IC<3>{});
+    step_epi(sb + 0, IC<0>{});
+    step_epi(sb + 1, IC<1>{});
+    step_epi(sb + 2, IC<2>{});
+    step_epi(sb + 3, IC<3>{});
   }
-  if (sb + 0 < total) step(sb + 0, IC<0>{});
-  if (sb + 1 < total) step(sb + 1, IC<1>{});
-  if (sb + 2 < total) step(sb + 2, IC<2>{});
+  if (sb + 0 < total) step_epi(sb + 0, IC<0>{});
+  if (sb + 1 < total) step_epi(sb + 1, IC<1>{});
+  if (sb + 2 < total) step_epi(sb + 2, IC<2>{});
+}
+
+template <bool A4, bool W4, bool SYM, bool CFG, int NB>
+__global__ __launch_bounds__(kThreads, 1) void k2_gemm(GemmArgs g) {
+  using Lay = Layout<A4, W4, NB>;
+  // One LDS object per ring stage: the compiler tracks DMA -> LDS writes per
+  // object, so a fragment read waits only for the DMA of its own stage.
+  __shared__ __attribute__((aligned(16))) uint8_t st0[Lay::kStage];
+  __shared__ __attribute__((aligned(16))) uint8_t st1[Lay::kStage];
+  __shared__ __attribute__((aligned(16))) uint8_t st2[Lay::kStage];
+  __shared__ __attribute__((aligned(16))) uint8_t st3[Lay::kStage];
+  static_assert(kStages == 4, "one LDS object per stage");
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // uniform
+  // waves w < NB - 8 also move weight pair w + 8 (NB is 8 or 9)
+  static_assert(NB == 8 || NB == 9, "wave roles");
+  if (wave < NB - 8)
+    gemm_wave<A4, W4, SYM, CFG, NB, 0, true>(g, wave, lane, st0, st1, st2, st3);
+  else if (wave < 4)
+    gemm_wave<A4, W4, SYM, CFG, NB, 0, false>(g, wave, lane, st0, st1, st2, st3);
+  else
+    gemm_wave<A4, W4, SYM, CFG, NB, 1, false>(g, wave, lane, st0, st1, st2, st3);
 }
 
 int g_cus = 0;  // compute units of the device (queried on first launch)
