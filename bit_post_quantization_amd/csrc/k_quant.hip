@@ -24,28 +24,48 @@ namespace ql {
 
 namespace {
 
+typedef unsigned v4u __attribute__((ext_vector_type(4)));
+typedef unsigned v2u __attribute__((ext_vector_type(2)));
+
 constexpr int kThreads = 256;
 constexpr int kWaves = kThreads / kWave;
-constexpr int kUnroll = 4;  // units per lane per iteration
+constexpr int kUnroll = 8;                        // units per lane per chunk
+constexpr int kChunk = kThreads * kUnroll;        // units per chunk
+constexpr int kQuantBlocks = 2048;                // grid cap of the quantizer
 
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes,
+                                           0x00020000);
+}
+
+// The kUnroll units of chunk `c` that this lane owns: unit c*kChunk + u*256 + tid.
+// Every load goes through a range-checked descriptor of the chunk (units past
+// the end of the tensor read as zeros), so all of them are issued back to back.
 template <bool BF16>
-__device__ __forceinline__ void load_unit(const void* X, int64_t idx, int64_t n, float (&e)[4]) {
-  if (idx < n) {
+__device__ __forceinline__ void load_chunk(const void* X, int64_t nunits, int64_t c,
+                                           float (&e)[kUnroll][4]) {
+  constexpr uint32_t kUnitBytes = BF16 ? 8 : 16;
+  const int64_t first = c * kChunk;
+  const int64_t left = nunits - first;
+  const uint32_t here = (uint32_t)(left < kChunk ? left : kChunk);
+  const __amdgpu_buffer_rsrc_t r =
+      buffer_rsrc(reinterpret_cast<const uint8_t*>(X) + first * kUnitBytes, here * kUnitBytes);
+#pragma unroll
+  for (int u = 0; u < kUnroll; ++u) {
+    const uint32_t off = (uint32_t)(u * kThreads + threadIdx.x) * kUnitBytes;
     if constexpr (BF16) {
-      const uint2 v = reinterpret_cast<const uint2*>(X)[idx];
-      e[0] = __uint_as_float(v.x << 16);
-      e[1] = __uint_as_float(v.x & 0xFFFF0000u);
-      e[2] = __uint_as_float(v.y << 16);
-      e[3] = __uint_as_float(v.y & 0xFFFF0000u);
+      const v2u v = __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0);
+      e[u][0] = __uint_as_float(v.x << 16);
+      e[u][1] = __uint_as_float(v.x & 0xFFFF0000u);
+      e[u][2] = __uint_as_float(v.y << 16);
+      e[u][3] = __uint_as_float(v.y & 0xFFFF0000u);
     } else {
-      const float4 v = reinterpret_cast<const float4*>(X)[idx];
-      e[0] = v.x;
-      e[1] = v.y;
-      e[2] = v.z;
-      e[3] = v.w;
+      const v4u v = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
+      e[u][0] = __uint_as_float(v.x);
+      e[u][1] = __uint_as_float(v.y);
+      e[u][2] = __uint_as_float(v.z);
+      e[u][3] = __uint_as_float(v.w);
     }
-  } else {
-    e[0] = e[1] = e[2] = e[3] = 0.0f;
   }
 }
 
@@ -54,12 +74,10 @@ __global__ __launch_bounds__(kThreads) void k1_reduce(QuantArgs a) {
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = threadIdx.x / kWave;
   uint32_t mp = 0, mn = 0;
-  const int64_t step = (int64_t)gridDim.x * kWaves * kWave * kUnroll;
-  for (int64_t base = ((int64_t)blockIdx.x * kWaves + wave) * kWave * kUnroll; base < a.nunits;
-       base += step) {
+  const int64_t nchunks = (a.nunits + kChunk - 1) / kChunk;
+  for (int64_t c = blockIdx.x; c < nchunks; c += gridDim.x) {
     float e[kUnroll][4];
-#pragma unroll
-    for (int u = 0; u < kUnroll; ++u) load_unit<BF16>(a.X, base + u * kWave + lane, a.nunits, e[u]);
+    load_chunk<BF16>(a.X, a.nunits, c, e);
     if constexpr (HB > 0) {
 #pragma unroll
       for (int u = 0; u < kUnroll; ++u) fwht_block<HB>(e[u], lane);
@@ -127,10 +145,36 @@ __device__ __forceinline__ void scales_from_partials(const QuantArgs& a, float& 
   }
 }
 
+// Codes of the four values of a unit; the same codes as quant_dual (round
+// half even of the correctly rounded quotient v / s, clamped), computed as
+// t = v * (1/s): the quotient and t differ by less than |t| * 2^-22, so
+// wherever t lies farther than |t| * 2^-20 + 2^-20 from every half-integer
+// both round to the same integer. Units with a value closer than that (and
+// non-finite t) are redone with the division; that is rare and
+// wave-uniform work is skipped when no lane needs it. With r = 0 for a zero
+// scale, t = 0 and the code is 0 as the definition requires; the sign of t
+// follows v, so one symmetric clamp serves both polarity regions.
+__device__ __forceinline__ void quant_unit(const float (&e)[4], float sp, float sn, float rp,
+                                           float rn, float qa, int (&c)[4]) {
+  bool slow = false;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const float v = e[i];
+    const float t = v * (v >= 0.0f ? rp : rn);
+    const float r = rintf(t);
+    const float z = fmaf(fabsf(t), 0x1p-20f, fabsf(t - r));
+    slow |= !(z < 0x1.fffcp-2f);  // 0.5 - 2^-19
+    c[i] = (int)__builtin_amdgcn_fmed3f(r, -qa, qa);
+  }
+  if (slow) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) c[i] = quant_dual(e[i], sp, sn, qa);
+  }
+}
+
 template <bool BF16, int HB, bool A4>
 __global__ __launch_bounds__(kThreads) void k1_quantize(QuantArgs a) {
   const int lane = threadIdx.x & (kWave - 1);
-  const int wave = threadIdx.x / kWave;
   float sp, sn;
   if (a.static_scales) {
     sp = a.static_scales[0];
@@ -142,50 +186,62 @@ __global__ __launch_bounds__(kThreads) void k1_quantize(QuantArgs a) {
     a.act_scales[0] = sp;
     a.act_scales[1] = sn;
   }
-  const int64_t step = (int64_t)gridDim.x * kWaves * kWave * kUnroll;
-  for (int64_t base = ((int64_t)blockIdx.x * kWaves + wave) * kWave * kUnroll; base < a.nunits;
-       base += step) {
+  const float rp = sp > 0.0f ? 1.0f / sp : 0.0f;
+  const float rn = sn > 0.0f ? 1.0f / sn : 0.0f;
+  constexpr uint32_t kCodeBytes = A4 ? 2 : 4;
+  const int64_t nchunks = (a.nunits + kChunk - 1) / kChunk;
+  for (int64_t ch = blockIdx.x; ch < nchunks; ch += gridDim.x) {
     float e[kUnroll][4];
-#pragma unroll
-    for (int u = 0; u < kUnroll; ++u) load_unit<BF16>(a.X, base + u * kWave + lane, a.nunits, e[u]);
+    load_chunk<BF16>(a.X, a.nunits, ch, e);
     if constexpr (HB > 0) {
 #pragma unroll
       for (int u = 0; u < kUnroll; ++u) fwht_block<HB>(e[u], lane);
     }
+    const int64_t first = ch * kChunk;
+    const int64_t left = a.nunits - first;
+    const uint32_t here = (uint32_t)(left < kChunk ? left : kChunk);
+    const __amdgpu_buffer_rsrc_t rc =
+        buffer_rsrc(reinterpret_cast<uint8_t*>(a.codes) + first * kCodeBytes, here * kCodeBytes);
 #pragma unroll
     for (int u = 0; u < kUnroll; ++u) {
-      const int64_t idx = base + u * kWave + lane;
       int c[4];
+      quant_unit(e[u], sp, sn, rp, rn, a.qa, c);
+      if (a.keep_mask != -1) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) c[i] = truncate_lsb(quant_dual(e[u][i], sp, sn, a.qa), a.keep_mask);
-      if (idx < a.nunits) {
-        if constexpr (A4) {
-          const uint32_t p = (c[0] & 0xF) | ((c[1] & 0xF) << 4) | ((c[2] & 0xF) << 8) |
-                             ((c[3] & 0xF) << 12);
-          reinterpret_cast<uint16_t*>(a.codes)[idx] = (uint16_t)p;
-        } else {
-          const uint32_t p = (c[0] & 0xFF) | ((c[1] & 0xFF) << 8) | ((c[2] & 0xFF) << 16) |
-                             ((uint32_t)(c[3] & 0xFF) << 24);
-          reinterpret_cast<uint32_t*>(a.codes)[idx] = p;
-        }
+        for (int i = 0; i < 4; ++i) c[i] = truncate_lsb(c[i], a.keep_mask);
+      }
+      const uint32_t off = (uint32_t)(u * kThreads + threadIdx.x) * kCodeBytes;
+      if constexpr (A4) {
+        const uint32_t p = (c[0] & 0xF) | ((c[1] & 0xF) << 4) | ((c[2] & 0xF) << 8) |
+                           ((c[3] & 0xF) << 12);
+        __builtin_amdgcn_raw_buffer_store_b16((unsigned short)p, rc, off, 0, 0);
+      } else {
+        const uint32_t p = (c[0] & 0xFF) | ((c[1] & 0xFF) << 8) | ((c[2] & 0xFF) << 16) |
+                           ((uint32_t)(c[3] & 0xFF) << 24);
+        __builtin_amdgcn_raw_buffer_store_b32(p, rc, off, 0, 0);
       }
     }
   }
 }
 
-int grid_for(int64_t nunits) {
-  const int64_t per_block = (int64_t)kThreads * kUnroll;
-  int64_t g = (nunits + per_block - 1) / per_block;
-  if (g > 2048) g = 2048;
-  if (g < 1) g = 1;
-  return (int)g;
+int chunks_of(int64_t nunits) {
+  const int64_t c = (nunits + kChunk - 1) / kChunk;
+  return (int)(c < 1 ? 1 : (c > (1 << 30) ? (1 << 30) : c));
+}
+
+// At most `cap` workgroups, each taking the same number of chunks (up to one
+// fewer for the last ones), so no workgroup runs a long tail alone.
+int balanced_grid(int nch, int cap) {
+  const int per = (nch + cap - 1) / cap;
+  return (nch + per - 1) / per;
 }
 
 template <bool BF16, int HB, bool A4>
 hipError_t run(QuantArgs a, hipStream_t s) {
-  const int g = grid_for(a.nunits);
+  const int nch = chunks_of(a.nunits);
+  const int g = balanced_grid(nch, kQuantBlocks);
   if (!a.static_scales) {
-    a.reduce_blocks = g < kMaxReduceBlocks ? g : kMaxReduceBlocks;
+    a.reduce_blocks = balanced_grid(nch, kMaxReduceBlocks);
     hipLaunchKernelGGL((k1_reduce<BF16, HB>), dim3(a.reduce_blocks), dim3(kThreads), 0, s, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
