@@ -161,6 +161,45 @@ def test_segments(torch, w_scale, seg):
                 x_dtype="bf16", tag="seg")
 
 
+@pytest.mark.parametrize("a_bits", [8, 4])
+def test_codes_at_rounding_boundaries(torch, a_bits):
+    """Values whose quotient by the scale lies on, or within a few ulps of, a
+    half-integer: the cases where a product with the reciprocal scale could
+    round differently from the IEEE quotient. Codes must match exactly."""
+    from bit_post_quantization_amd import QuantLinear
+    qa = 127 if a_bits == 8 else 7
+    mx, mn = np.float32(100.0), np.float32(50.0)
+    sp, sn = mx / np.float32(qa), mn / np.float32(qa)
+    vals = []
+    for k in range(qa + 1):
+        for sgn, s in ((1.0, sp), (-1.0, sn)):
+            c = np.float32(sgn * (k + 0.5)) * s
+            for d in range(-4, 5):
+                v = c
+                step = np.float32(np.inf) if d > 0 else np.float32(-np.inf)
+                for _ in range(abs(d)):
+                    v = np.nextafter(v, step)
+                vals.append(v)
+    vals = np.asarray(vals, np.float32)
+    vals = vals[(vals <= mx) & (vals >= -mn)]
+    K = 256
+    M = 2 * ((vals.size + K - 1) // K + 1)
+    X = synth.random_int_codes(3, "bnd/X", (M, K), -40, 40).astype(np.float32) * np.float32(0.5)
+    flat = X.reshape(-1)
+    flat[: vals.size] = vals
+    flat[-1], flat[-2] = mx, -mn
+    W = synth.weight_normal(3, "bnd/W", 64, K)
+    ql = QuantLinear(_dev(torch, W), w_bits=8, a_bits=a_bits)
+    codes_d, s_d = ql.quantize(_dev(torch, X))
+    torch.cuda.synchronize()
+    s_g = s_d.cpu().numpy()
+    assert np.array_equal(s_g, np.array([sp, sn], np.float32)), s_g
+    codes_g = unpack_codes(codes_d.cpu().numpy(), K, a_bits)
+    codes_o = oracle.quantize_act(X, s_g, a_bits, 0)
+    bad = np.nonzero(codes_g.reshape(-1) != codes_o.reshape(-1))[0]
+    assert bad.size == 0, f"{bad.size} codes differ, first at {bad[:5]}: x={flat[bad[:5]]}"
+
+
 def test_static_scales(torch):
     M, K, N = 64, 256, 80
     X = synth.silu_normal(4, "static/X", M, K)
