@@ -73,7 +73,7 @@ template <bool BF16, int HB>
 __global__ __launch_bounds__(kThreads) void k1_reduce(QuantArgs a) {
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = threadIdx.x / kWave;
-  uint32_t mp = 0, mn = 0;
+  uint32_t mp = 0, mn = 0x80000000u;
   const int64_t nchunks = (a.nunits + kChunk - 1) / kChunk;
   for (int64_t c = blockIdx.x; c < nchunks; c += gridDim.x) {
     float e[kUnroll][4];
@@ -82,16 +82,20 @@ __global__ __launch_bounds__(kThreads) void k1_reduce(QuantArgs a) {
 #pragma unroll
       for (int u = 0; u < kUnroll; ++u) fwht_block<HB>(e[u], lane);
     }
+    // On the bit patterns: non-negative floats order like their bits as
+    // signed integers (negative floats are negative integers), and negative
+    // floats order by magnitude like their bits as unsigned integers above
+    // 0x80000000 (non-negative floats lie below it). One integer max each.
 #pragma unroll
     for (int u = 0; u < kUnroll; ++u)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const float v = e[u][i];
-        const uint32_t b = __float_as_uint(v) & 0x7FFFFFFFu;
-        mp = (v > 0.0f && b > mp) ? b : mp;
-        mn = (v < 0.0f && b > mn) ? b : mn;
+        const uint32_t b = __float_as_uint(e[u][i]);
+        mp = (uint32_t)max((int32_t)mp, (int32_t)b);
+        mn = max(mn, b);
       }
   }
+  mn &= 0x7FFFFFFFu;  // magnitude of the most negative value (0 if none)
   mp = wave_max_u32(mp);
   mn = wave_max_u32(mn);
   __shared__ uint32_t sm[2][kWaves];
