@@ -195,20 +195,44 @@ __device__ __forceinline__ float epi(int accp, int accn, float sp, float sn, flo
   return __fmul_rn(y, inv_b);
 }
 
-// Tiles of workgroup b: XCD-banded when both counts divide by 8, else strided.
+// Tiles of workgroup b. When grid and tile counts divide by 8, each XCD
+// (workgroup id mod 8) owns a band of consecutive tiles. When that band is
+// R whole tile rows and its per_x workgroups divide into R rows of C
+// columns, the workgroups run the band as successive R x C blocks (all R
+// rows, C columns at a time): the concurrent tiles of an XCD then share R
+// activation row panels and C weight column panels in its L2, instead of
+// streaming every weight column panel once per row. Otherwise tiles are
+// taken in row-major order within the band, or strided over the grid.
 struct TileList {
   int first, stride, count;
-  __device__ __forceinline__ int at(int i) const { return first + i * stride; }
+  int ct, C;  // grouped order: tile columns, block width (C = 0: linear order)
+  int row0, r, c;
+  __device__ __forceinline__ int at(int i) const {
+    if (C) return (row0 + r) * ct + i * C + c;
+    return first + i * stride;
+  }
 };
 
-__device__ __forceinline__ TileList my_tiles(int T) {
+__device__ __forceinline__ TileList my_tiles(int T, int ct) {
   const int G = gridDim.x, b = blockIdx.x;
   TileList L;
+  L.C = 0;
+  L.ct = ct;
   if ((G & 7) == 0 && (T & 7) == 0) {
     const int x = b & 7, j = b >> 3, per_x = G >> 3, band = T >> 3;
     L.first = x * band + j;
     L.stride = per_x;
     L.count = j < band ? (band - j + per_x - 1) / per_x : 0;
+    if (band % ct == 0 && band % per_x == 0) {
+      const int R = band / ct;
+      if (per_x % R == 0 && ct % (per_x / R) == 0) {
+        L.C = per_x / R;
+        L.row0 = x * R;
+        L.r = j / L.C;
+        L.c = j % L.C;
+        L.count = band / per_x;
+      }
+    }
   } else {
     L.first = b;
     L.stride = G;
@@ -293,7 +317,7 @@ __device__ __forceinline__ void gemm_wave(const GemmArgs& g, int wave, int lane,
 
   const int ct = (g.N + BN - 1) / BN;
   const int T = (((CFG ? g.Mh : g.M) + RPT - 1) / RPT) * ct;
-  const TileList tl = my_tiles(T);
+  const TileList tl = my_tiles(T, ct);
   if (tl.count == 0) return;
 
   const int nk = (g.K + BK - 1) / BK;
