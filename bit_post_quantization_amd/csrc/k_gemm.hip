@@ -31,10 +31,13 @@
 //    consecutive tiles that share rows in that XCD's L2.
 //  * Every out-of-range row or K-chunk is read as zero by the buffer range
 //    check, so ragged M, N and K need no special path.
-//  * 4-bit codes stay packed through memory and LDS and are unpacked on the
-//    way into the MFMA, each code multiplied by 16 (nibble placed in the high
-//    half of its byte: two ANDs, a shift, two byte permutes); accumulators
-//    are shifted back exactly in the epilogue.
+//  * 4-bit activation codes stay packed through memory and LDS and are
+//    unpacked on the way into the MFMA, each code multiplied by 16 (nibble
+//    placed in the high half of its byte: two ANDs, a shift, two byte
+//    permutes); accumulators are shifted back exactly in the epilogue.
+//    4-bit weight codes arrive already expanded to one int8 per code (the
+//    plan stores them so): the kernel is bound by its MFMA and VALU issue,
+//    not by weight bytes, so the per-step weight unpack is not worth it.
 //  * CFG pairing: a row band is 16 conditional rows and their 16
 //    unconditional partners (fragments 0 and 1), so a lane holds both
 //    accumulators of a pair in the same register slot.
@@ -134,18 +137,18 @@ struct FragIO {
   }
 };
 
-template <bool A4, bool W4, int NB>
+template <bool A4, int NB>
 struct Layout {
   static constexpr int kNB0 = (NB + 1) / 2;  // weight fragments of column group 0
   static constexpr int kNB1 = NB / 2;        // weight fragments of column group 1
   static constexpr int kAFrags = 8;          // 128 rows = 8 fragment pairs
   static constexpr int kABytes = kAFrags * FragIO<A4>::kBytes;
-  static constexpr int kStage = kABytes + NB * FragIO<W4>::kBytes;
+  static constexpr int kStage = kABytes + NB * FragIO<false>::kBytes;
   // DMA: wave w moves activation pair w and weight pair w, and waves
   // w < NB - 8 also weight pair w + 8.
   static_assert(NB >= 8 && NB <= 16, "fragment distribution");
-  static constexpr int kOpsLow = FragIO<A4>::kLoads + 2 * FragIO<W4>::kLoads;  // waves < NB-8
-  static constexpr int kOpsHigh = FragIO<A4>::kLoads + FragIO<W4>::kLoads;     // the others
+  static constexpr int kOpsLow = FragIO<A4>::kLoads + 2 * FragIO<false>::kLoads;  // waves < NB-8
+  static constexpr int kOpsHigh = FragIO<A4>::kLoads + FragIO<false>::kLoads;     // the others
 };
 
 // MFMA operand (16 int8 in natural K order) from raw fragment data.
@@ -299,14 +302,14 @@ __device__ __forceinline__ void schedule_step() {
 // pair w + 8, so a step's body has no branches and every step issues the
 // same number of loads: the compiler can then prove from the explicit
 // waits below that each LDS read finds its data landed.
-template <bool A4, bool W4, bool SYM, bool CFG, int NB, int CG, bool TW>
+template <bool A4, bool SYM, bool CFG, int NB, int CG, bool TW>
 __device__ __forceinline__ void gemm_wave(const GemmArgs& g, int wave, int lane, uint8_t* st0,
                                           uint8_t* st1, uint8_t* st2, uint8_t* st3) {
-  using Lay = Layout<A4, W4, NB>;
+  using Lay = Layout<A4, NB>;
   using IA = FragIO<A4>;
-  using IW = FragIO<W4>;
+  using IW = FragIO<false>;  // weights are int8 codes (4-bit ones expanded by the plan)
   constexpr int NP = SYM ? 1 : 2;                     // accumulator planes
-  constexpr int SHIFT = (A4 ? 4 : 0) + (W4 ? 4 : 0);  // undo the x16 unpack
+  constexpr int SHIFT = A4 ? 4 : 0;  // undo the x16 unpack of 4-bit activations
   constexpr int BN = 16 * NB;
   constexpr int NBW = CG ? Lay::kNB1 : Lay::kNB0;     // weight fragments of this wave
   constexpr int J0 = CG ? Lay::kNB0 : 0;              // first weight fragment of this wave
@@ -378,7 +381,7 @@ __device__ __forceinline__ void gemm_wave(const GemmArgs& g, int wave, int lane,
   auto issue = [&](uint8_t* slot) __attribute__((always_inline)) {
     const int k0 = iss_k * BK;
     const unsigned sa = (unsigned)k0 / (A4 ? 2u : 1u);
-    const unsigned sw = (unsigned)k0 / (W4 ? 2u : 1u);
+    const unsigned sw = (unsigned)k0;
     const bool ragged = k0 + BK > g.K;  // chunks past K must read zeros
 #pragma unroll
     for (int i = 0; i < IA::kLoads; ++i) {
@@ -427,7 +430,7 @@ __device__ __forceinline__ void gemm_wave(const GemmArgs& g, int wave, int lane,
 
   struct Frags {
     Frag<A4> a[2][2];    // [pair of the band][half]
-    Frag<W4> w[NBW][2];  // [fragment slot][half]
+    Frag<false> w[NBW][2];  // [fragment slot][half]
   };
   Frags F[2];
   auto read_all = [&](Frags& f, const uint8_t* slot) __attribute__((always_inline)) {
@@ -461,7 +464,7 @@ __device__ __forceinline__ void gemm_wave(const GemmArgs& g, int wave, int lane,
 #pragma unroll
     for (int jj = 0; jj < NBW; ++jj)
 #pragma unroll
-      for (int h = 0; h < 2; ++h) b[jj][h] = operand<W4>(f.w[jj][h]);
+      for (int h = 0; h < 2; ++h) b[jj][h] = operand<false>(f.w[jj][h]);
 #pragma unroll
     for (int h = 0; h < 2; ++h)
 #pragma unroll
@@ -476,7 +479,7 @@ __device__ __forceinline__ void gemm_wave(const GemmArgs& g, int wave, int lane,
         }
       }
     constexpr int kReads = 4 + 2 * NBW;
-    constexpr int kValu = (SYM ? 0 : 12) + (A4 ? 10 : 0) + (W4 ? (10 * NBW + 1) / 2 : 0);
+    constexpr int kValu = (SYM ? 0 : 12) + (A4 ? 10 : 0);
     schedule_step<NBW, kReads, kValu, !SYM>();
   };
 
@@ -625,9 +628,9 @@ __device__ __forceinline__ void gemm_wave(const GemmArgs& g, int wave, int lane,
   if (sb + 2 < total) step_epi(sb + 2, IC<2>{});
 }
 
-template <bool A4, bool W4, bool SYM, bool CFG, int NB>
+template <bool A4, bool SYM, bool CFG, int NB>
 __global__ __launch_bounds__(kThreads, 1) void k2_gemm(GemmArgs g) {
-  using Lay = Layout<A4, W4, NB>;
+  using Lay = Layout<A4, NB>;
   // One LDS object per ring stage: the compiler tracks DMA -> LDS writes per
   // object, so a fragment read waits only for the DMA of its own stage.
   __shared__ __attribute__((aligned(16))) uint8_t st0[Lay::kStage];
@@ -640,16 +643,16 @@ __global__ __launch_bounds__(kThreads, 1) void k2_gemm(GemmArgs g) {
   // waves w < NB - 8 also move weight pair w + 8 (NB is 8 or 9)
   static_assert(NB == 8 || NB == 9, "wave roles");
   if (wave < NB - 8)
-    gemm_wave<A4, W4, SYM, CFG, NB, 0, true>(g, wave, lane, st0, st1, st2, st3);
+    gemm_wave<A4, SYM, CFG, NB, 0, true>(g, wave, lane, st0, st1, st2, st3);
   else if (wave < 4)
-    gemm_wave<A4, W4, SYM, CFG, NB, 0, false>(g, wave, lane, st0, st1, st2, st3);
+    gemm_wave<A4, SYM, CFG, NB, 0, false>(g, wave, lane, st0, st1, st2, st3);
   else
-    gemm_wave<A4, W4, SYM, CFG, NB, 1, false>(g, wave, lane, st0, st1, st2, st3);
+    gemm_wave<A4, SYM, CFG, NB, 1, false>(g, wave, lane, st0, st1, st2, st3);
 }
 
 int g_cus = 0;  // compute units of the device (queried on first launch)
 
-template <bool A4, bool W4, bool SYM, bool CFG, int NB>
+template <bool A4, bool SYM, bool CFG, int NB>
 hipError_t run(const GemmArgs& g, hipStream_t s) {
   const int rpt = CFG ? 64 : 128;
   const int T = (((CFG ? g.Mh : g.M) + rpt - 1) / rpt) * ((g.N + 16 * NB - 1) / (16 * NB));
@@ -661,28 +664,27 @@ hipError_t run(const GemmArgs& g, hipStream_t s) {
     g_cus = cus;
   }
   const int G = T < g_cus ? T : g_cus;
-  hipLaunchKernelGGL((k2_gemm<A4, W4, SYM, CFG, NB>), dim3(G), dim3(kThreads), 0, s, g);
+  hipLaunchKernelGGL((k2_gemm<A4, SYM, CFG, NB>), dim3(G), dim3(kThreads), 0, s, g);
   return hipGetLastError();
 }
 
-template <bool A4, bool W4, bool SYM, bool CFG>
+template <bool A4, bool SYM, bool CFG>
 hipError_t run_nb(const GemmArgs& g, hipStream_t s) {
   // 144-column tiles when they divide N, else 128.
-  if (g.N % 144 == 0) return run<A4, W4, SYM, CFG, 9>(g, s);
-  return run<A4, W4, SYM, CFG, 8>(g, s);
+  if (g.N % 144 == 0) return run<A4, SYM, CFG, 9>(g, s);
+  return run<A4, SYM, CFG, 8>(g, s);
 }
 
-template <bool A4, bool W4>
+template <bool A4>
 hipError_t run_mode(const GemmArgs& g, int sym, int cfg, hipStream_t s) {
-  if (sym) return cfg ? run_nb<A4, W4, true, true>(g, s) : run_nb<A4, W4, true, false>(g, s);
-  return cfg ? run_nb<A4, W4, false, true>(g, s) : run_nb<A4, W4, false, false>(g, s);
+  if (sym) return cfg ? run_nb<A4, true, true>(g, s) : run_nb<A4, true, false>(g, s);
+  return cfg ? run_nb<A4, false, true>(g, s) : run_nb<A4, false, false>(g, s);
 }
 
 }  // namespace
 
-hipError_t launch_gemm(const GemmArgs& g, int a4, int w4, int sym, int cfg, hipStream_t s) {
-  if (a4) return w4 ? run_mode<true, true>(g, sym, cfg, s) : run_mode<true, false>(g, sym, cfg, s);
-  return w4 ? run_mode<false, true>(g, sym, cfg, s) : run_mode<false, false>(g, sym, cfg, s);
+hipError_t launch_gemm(const GemmArgs& g, int a4, int sym, int cfg, hipStream_t s) {
+  return a4 ? run_mode<true>(g, sym, cfg, s) : run_mode<false>(g, sym, cfg, s);
 }
 
 }  // namespace ql

@@ -78,8 +78,8 @@ __device__ __forceinline__ int quant_sym(float v, float s, float q) {
   return s > 0.0f ? (int)r : 0;
 }
 
-// Codes of 4 consecutive weights of one row per thread (K % 4 == 0).
-template <bool W4>
+// Codes of 4 consecutive weights of one row per thread (K % 4 == 0), one
+// int8 per code for both widths (4-bit codes lie in [-7, 7]).
 __global__ __launch_bounds__(256) void k0_quant_w(const float* W, const float* sw, int K,
                                                   int64_t nunits, float qw, uint8_t* out) {
   const int64_t u = (int64_t)blockIdx.x * 256 + threadIdx.x;
@@ -89,28 +89,9 @@ __global__ __launch_bounds__(256) void k0_quant_w(const float* W, const float* s
   const float4 v = reinterpret_cast<const float4*>(W)[u];
   const int c0 = quant_sym(v.x, s, qw), c1 = quant_sym(v.y, s, qw);
   const int c2 = quant_sym(v.z, s, qw), c3 = quant_sym(v.w, s, qw);
-  if constexpr (W4) {
-    reinterpret_cast<uint16_t*>(out)[u] =
-        (uint16_t)((c0 & 0xF) | ((c1 & 0xF) << 4) | ((c2 & 0xF) << 8) | ((c3 & 0xF) << 12));
-  } else {
-    reinterpret_cast<uint32_t*>(out)[u] =
-        (uint32_t)(c0 & 0xFF) | ((uint32_t)(c1 & 0xFF) << 8) | ((uint32_t)(c2 & 0xFF) << 16) |
-        ((uint32_t)(c3 & 0xFF) << 24);
-  }
-}
-
-// Plan codes -> int8 [N,K] (sign-extended nibbles for 4-bit plans).
-template <bool W4>
-__global__ __launch_bounds__(256) void k0_unpack(const uint8_t* in, int64_t n_elems, int8_t* out) {
-  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (i >= n_elems) return;
-  if constexpr (W4) {
-    const int b = in[i >> 1];
-    int v = (i & 1) ? (b >> 4) & 0xF : b & 0xF;
-    out[i] = (int8_t)(v >= 8 ? v - 16 : v);
-  } else {
-    out[i] = (int8_t)in[i];
-  }
+  reinterpret_cast<uint32_t*>(out)[u] =
+      (uint32_t)(c0 & 0xFF) | ((uint32_t)(c1 & 0xFF) << 8) | ((uint32_t)(c2 & 0xFF) << 16) |
+      ((uint32_t)(c3 & 0xFF) << 24);
 }
 
 // K3: out = yu + w * (yc - yu); yc = Y[e], yu = Y[e + half].
@@ -162,25 +143,11 @@ hipError_t launch_weight_scales(const uint32_t* rowmax, int N, int mode, const i
   return hipGetLastError();
 }
 
-hipError_t launch_quantize_weights(const float* W, const float* sw, int N, int K, int w4, float qw,
+hipError_t launch_quantize_weights(const float* W, const float* sw, int N, int K, float qw,
                                    uint8_t* out, hipStream_t s) {
   const int64_t nunits = (int64_t)N * K / 4;
-  const dim3 grid(blocks_for(nunits, 256));
-  if (w4)
-    hipLaunchKernelGGL((k0_quant_w<true>), grid, dim3(256), 0, s, W, sw, K, nunits, qw, out);
-  else
-    hipLaunchKernelGGL((k0_quant_w<false>), grid, dim3(256), 0, s, W, sw, K, nunits, qw, out);
-  return hipGetLastError();
-}
-
-hipError_t launch_unpack_weights(const uint8_t* in, int N, int K, int w4, int8_t* out,
-                                 hipStream_t s) {
-  const int64_t n = (int64_t)N * K;
-  const dim3 grid(blocks_for(n, 256));
-  if (w4)
-    hipLaunchKernelGGL((k0_unpack<true>), grid, dim3(256), 0, s, in, n, out);
-  else
-    hipLaunchKernelGGL((k0_unpack<false>), grid, dim3(256), 0, s, in, n, out);
+  hipLaunchKernelGGL(k0_quant_w, dim3(blocks_for(nunits, 256)), dim3(256), 0, s, W, sw, K, nunits,
+                     qw, out);
   return hipGetLastError();
 }
 

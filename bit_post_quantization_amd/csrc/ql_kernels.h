@@ -29,7 +29,7 @@ struct QuantArgs {
 
 struct GemmArgs {
   const uint8_t* A;          // activation codes: int8 [M,K] or packed [M,K/2]
-  const uint8_t* W;          // weight codes: int8 [N,K] or packed [N,K/2]
+  const uint8_t* W;          // weight codes: int8 [N,K] (4-bit codes expanded)
   const float* act_scales;   // [2]
   const float* w_scales;     // [N]
   float* Y;                  // [M,N] or [M/2,N]
@@ -46,7 +46,7 @@ hipError_t launch_quantize(const QuantArgs& a, int x_bf16, int hadamard_block, i
                            hipStream_t s);
 
 // K2: GEMM + epilogue.
-hipError_t launch_gemm(const GemmArgs& g, int a4, int w4, int sym, int cfg, hipStream_t s);
+hipError_t launch_gemm(const GemmArgs& g, int a4, int sym, int cfg, hipStream_t s);
 
 // K3: standalone CFG combine.
 hipError_t launch_cfg_combine(const float* Y, int64_t half_elems, float w, float* out,
@@ -57,9 +57,7 @@ hipError_t launch_rotate_rows(float* W, int64_t nunits, int hadamard_block, hipS
 hipError_t launch_row_absmax(const float* W, int N, int K, uint32_t* rowmax, hipStream_t s);
 hipError_t launch_weight_scales(const uint32_t* rowmax, int N, int mode, const int32_t* seg,
                                 int nseg, float qw, float* sw, hipStream_t s);
-hipError_t launch_quantize_weights(const float* W, const float* sw, int N, int K, int w4,
-                                   float qw, uint8_t* out, hipStream_t s);
-hipError_t launch_unpack_weights(const uint8_t* in, int N, int K, int w4, int8_t* out,
-                                 hipStream_t s);
+hipError_t launch_quantize_weights(const float* W, const float* sw, int N, int K, float qw,
+                                   uint8_t* out, hipStream_t s);
 
 }  // namespace ql

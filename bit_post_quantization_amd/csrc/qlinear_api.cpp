@@ -133,7 +133,9 @@ ql_status qlinear_plan(const ql_desc* d, const float* W, void* stream, qlinear_p
     return fail(QL_ERR_HIP, "hipGetDevice failed");
   }
   const int64_t N = d->N, K = d->K;
-  const size_t wbytes = (size_t)(d->w_bits == 4 ? N * K / 2 : N * K);
+  // Weight codes are stored one per byte for both widths (4-bit codes lie
+  // in [-7, 7]); the GEMM reads them without an unpack step.
+  const size_t wbytes = (size_t)(N * K);
   float* rot = nullptr;
   uint32_t* rowmax = nullptr;
   int32_t* segd = nullptr;
@@ -180,7 +182,7 @@ ql_status qlinear_plan(const ql_desc* d, const float* W, void* stream, qlinear_p
   QL_TRY(ql::launch_row_absmax(src, (int)N, (int)K, rowmax, s), "weight row maxima");
   QL_TRY(ql::launch_weight_scales(rowmax, (int)N, mode, segd, ngroups, qw, p->sw, s),
          "weight scales");
-  QL_TRY(ql::launch_quantize_weights(src, p->sw, (int)N, (int)K, d->w_bits == 4, qw, p->wq, s),
+  QL_TRY(ql::launch_quantize_weights(src, p->sw, (int)N, (int)K, qw, p->wq, s),
          "weight codes");
   QL_TRY(hipStreamSynchronize(s), "synchronising plan stream");
 #undef QL_TRY
@@ -200,8 +202,8 @@ ql_status qlinear_plan_weights(qlinear_plan_t p, int8_t* w_codes, float* w_scale
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   hipError_t e;
   if (w_codes) {
-    e = ql::launch_unpack_weights(p->wq, p->d.N, p->d.K, p->d.w_bits == 4, w_codes, s);
-    if (e != hipSuccess) return hip_fail(e, "unpacking weight codes");
+    e = hipMemcpyAsync(w_codes, p->wq, (size_t)p->d.N * p->d.K, hipMemcpyDeviceToDevice, s);
+    if (e != hipSuccess) return hip_fail(e, "copying weight codes");
   }
   if (w_scales) {
     e = hipMemcpyAsync(w_scales, p->sw, (size_t)p->d.N * sizeof(float), hipMemcpyDeviceToDevice, s);
@@ -267,12 +269,12 @@ ql_status qlinear_gemm(qlinear_plan_t p, const void* codes, const float* act_sca
   g.K = p->d.K;
   g.Mh = cfg ? M / 2 : M;
   g.lda = p->d.a_bits == 4 ? p->d.K / 2 : p->d.K;
-  g.ldw = p->d.w_bits == 4 ? p->d.K / 2 : p->d.K;
+  g.ldw = p->d.K;
   if ((int64_t)M * g.lda >= ((int64_t)1 << 31) || (int64_t)g.N * g.ldw >= ((int64_t)1 << 31))
     return fail(QL_ERR_UNSUPPORTED, "codes or weights of 2 GiB or more (M = %d)", M);
   g.guidance = w;
   g.inv_b = p->d.hadamard_block ? 1.0f / (float)p->d.hadamard_block : 1.0f;
-  hipError_t e = ql::launch_gemm(g, p->d.a_bits == 4, p->d.w_bits == 4,
+  hipError_t e = ql::launch_gemm(g, p->d.a_bits == 4,
                                  p->d.a_scale_mode == QL_ASCALE_SYMMETRIC, cfg,
                                  reinterpret_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "launching gemm");

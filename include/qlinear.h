@@ -95,8 +95,10 @@ typedef struct {
  * butterfly distance 1, 2, ..., B/2, each (a,b) -> (a+b, a-b) in fp32), take
  * the symmetric absmax weight scale per channel / segment / tensor
  * (s = absmax / qmax_w, qmax_w = 2^(w_bits-1) - 1), quantize
- * (round half to even, clamp to [-qmax_w, qmax_w]) and pack 4-bit codes two
- * per byte (element 2j in bits 0-3 and 2j+1 in bits 4-7 of byte j).
+ * (round half to even, clamp to [-qmax_w, qmax_w]). The plan keeps one
+ * signed byte per weight code for both widths (4-bit codes lie in [-7, 7]):
+ * the GEMM is bound by its matrix-core and vector issue, not by weight bytes,
+ * so it reads 4-bit weights without an unpack step.
  *   d   : HOST descriptor (copied; seg_offsets copied too).
  *   W   : DEVICE fp32 [N,K]; read only, may be freed after the call.
  *   out : HOST; receives the plan handle.
@@ -111,8 +113,8 @@ ql_status qlinear_plan(const ql_desc* d, const float* W, void* stream, qlinear_p
 ql_status qlinear_plan_destroy(qlinear_plan_t p);
 
 /* Copy a plan's weights out for inspection: w_codes DEVICE int8 [N,K]
- * (unpacked, one code per byte), w_scales DEVICE fp32 [N]. Either may be
- * NULL to skip it. */
+ * (one code per byte), w_scales DEVICE fp32 [N]. Either may be NULL to skip
+ * it. */
 ql_status qlinear_plan_weights(qlinear_plan_t p, int8_t* w_codes, float* w_scales, void* stream);
 
 /*
@@ -130,7 +132,8 @@ ql_status qlinear_plan_weights(qlinear_plan_t p, int8_t* w_codes, float* w_scale
  *   lsb_k         : 0 <= lsb_k < a_bits.
  *   static_scales : DEVICE fp32 [2] {s+, s-}, or NULL for dynamic scales.
  *   codes         : DEVICE out: int8 [M,K] (a_bits 8) or uint8 [M,K/2]
- *                   packed as above (a_bits 4).
+ *                   (a_bits 4), two 4-bit two's-complement codes per byte:
+ *                   element 2j in bits 0-3 and 2j+1 in bits 4-7 of byte j.
  *   act_scales    : DEVICE out fp32 [2] {s+, s-} used for the codes.
  */
 ql_status qlinear_quantize_act(qlinear_plan_t p, const void* X, int32_t M, int32_t lsb_k,
