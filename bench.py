@@ -37,7 +37,7 @@ def parse():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=50)
     p.add_argument("--warmup", type=int, default=10)
-    p.add_argument("--workload", default="mlp", help="mlp (default) | block | c3 | c4 | c5")
+    p.add_argument("--workload", default="mlp", help="mlp (default) | block | c3 | c4 | c5 | c6")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=12.0,
                    help="approximate CPU time budget of the oracle baseline")
@@ -239,6 +239,114 @@ def bench_tasq_sweep(torch, args):
     print(json.dumps(out), flush=True)
 
 
+def bench_tasq_weight_sweep(torch, args):
+    """TASQ on the weight side: the same 112 DiT-XL/2 linears per step, each
+    with ONE stored W8 plan and one operating view of it. The 50 steps fall in
+    4 stages; at a stage change every view whose depth changes is rewritten
+    from its stored plan (qlinear_plan_lsb_update, inside the timed region).
+    Activations are quantized at per-step static scales from a table that an
+    untimed calibration pass fills with the dynamic scales of a separate
+    seeded batch (one quantize pass instead of two in the timed region)."""
+    from bit_post_quantization_amd import (QuantLinear, qlinear_gemm, qlinear_plan_lsb_update,
+                                           qlinear_quantize_act)
+    from workloads import configs
+    wl = configs.WORKLOADS["c6"]
+    wsch = configs.c6_w_schedule()
+    steps = min(args.steps, wl.steps)
+    g = torch.Generator(device="cuda")
+    g.manual_seed(6)
+    M = wl.M
+    bases, views, pool, calib, ys = [], [], {}, {}, {}
+    for li, L in enumerate(wl.layers):
+        W = torch.randn(L.N, L.K, device="cuda", generator=g) * 0.02
+        bases.append(QuantLinear(W))
+        del W
+        views.append(bases[-1].lsb_view(int(wsch[0, li])))
+        if L.K not in pool:
+            pool[L.K] = [torch.nn.functional.silu(torch.randn(M, L.K, device="cuda", generator=g))
+                         for _ in range(4)]
+            calib[L.K] = [torch.nn.functional.silu(torch.randn(M, L.K, device="cuda",
+                                                               generator=g)) for _ in range(4)]
+        if L.N not in ys:
+            ys[L.N] = torch.empty(M // 2, L.N, dtype=torch.float32, device="cuda")
+    codes = {}
+    for L, ql in zip(wl.layers, bases):
+        if L.K not in codes:
+            codes[L.K] = ql.alloc_codes(M)
+    scales = torch.empty(2, dtype=torch.float32, device="cuda")
+    # Calibration: per-step, per-layer static scale table [steps, layers, 2].
+    table = torch.empty(wl.steps, len(wl.layers), 2, dtype=torch.float32, device="cuda")
+    for t in range(wl.steps):
+        for li, (L, ql) in enumerate(zip(wl.layers, bases)):
+            qlinear_quantize_act(ql.plan, calib[L.K][(t + 2 * li) % 4], M, 0, None, codes[L.K],
+                                 table[t, li])
+    torch.cuda.synchronize()
+    ops_per_step = sum(4.0 * M * L.N * L.K for L in wl.layers)
+    depth = [int(wsch[0, li]) for li in range(len(wl.layers))]
+    n_updates = [0]
+
+    def set_stage(grp):
+        for li in range(len(wl.layers)):
+            k = int(wsch[grp, li])
+            if k != depth[li]:
+                qlinear_plan_lsb_update(views[li].plan, bases[li].plan, k)
+                depth[li] = k
+                n_updates[0] += 1
+
+    def step(t):
+        set_stage(configs.stage_of(wl, t))
+        for li, (L, v) in enumerate(zip(wl.layers, views)):
+            X = pool[L.K][(t + li) % 4]
+            qlinear_quantize_act(v.plan, X, M, 0, table[t, li], codes[L.K], scales)
+            qlinear_gemm(v.plan, codes[L.K], scales, M, 1, L.guidance, ys[L.N])
+
+    # Cost of one full rewrite of all 112 views (measured apart, untimed).
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for li in range(len(wl.layers)):
+        qlinear_plan_lsb_update(views[li].plan, bases[li].plan, int(wsch[1, li]))
+    e1.record()
+    torch.cuda.synchronize()
+    rewrite_all_ms = e0.elapsed_time(e1)
+    for li in range(len(wl.layers)):
+        depth[li] = int(wsch[1, li])
+    for t in range(min(args.warmup, steps)):
+        step(t)
+    set_stage(0)
+    n_updates[0] = 0
+    torch.cuda.synchronize()
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+    evs[0].record()
+    for t in range(steps):
+        step(t)
+        evs[t + 1].record()
+    torch.cuda.synchronize()
+    per = np.array([evs[t].elapsed_time(evs[t + 1]) for t in range(steps)])
+    total_ms = float(per.sum())
+    wbytes = sum(L.N * L.K for L in wl.layers)
+    out = {
+        "metric": "quantized-linear int8 TOPS (% MFMA peak), TASQ weight-side 50-step sweep",
+        "value": round(ops_per_step * steps / (total_ms * 1e-3) / 1e12, 2), "unit": "TOPS",
+        "n_gpus": 1, "steps": steps, "warmup": min(args.warmup, steps),
+        "ms_per_step": round(total_ms / steps, 4), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "int8",
+        "data": "synthetic (device-generated, seeded: X = SiLU(N(0,1)), W ~ N(0, 0.02^2))",
+        "config": {"workload": "TASQ weight-side sweep: 28 DiT-XL/2 blocks x (qkv, proj, fc1, "
+                               "fc2), W8 storage, per-(stage, layer) weight depth in {0,2,4} over "
+                               "4 stages, A8 DualScale at per-step static scales, CFG w=4",
+                   "M": M, "linears_per_step": len(wl.layers), "stages": wl.stages},
+        "per_step_tops": {"min": round(ops_per_step / (per.max() * 1e-3) / 1e12, 1),
+                          "median": round(ops_per_step / (np.median(per) * 1e-3) / 1e12, 1),
+                          "max": round(ops_per_step / (per.min() * 1e-3) / 1e12, 1)},
+        "view_rewrites_timed": n_updates[0],
+        "rewrite_all_views_ms": round(rewrite_all_ms, 4),
+        "rewrite_all_views_GBps": round(2.0 * wbytes / (rewrite_all_ms * 1e-3) / 1e9, 1),
+        "weight_bytes_stored_plus_views": 2 * wbytes,
+        "mfma_ops_per_step": ops_per_step,
+    }
+    print(json.dumps(out), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -253,6 +361,9 @@ def main():
 
     if args.workload == "c5":
         bench_tasq_sweep(torch, args)
+        return
+    if args.workload == "c6":
+        bench_tasq_weight_sweep(torch, args)
         return
     wl, Ls = layers_for(args.workload)
     layers = [Layer(torch, wl, L) for L in Ls]

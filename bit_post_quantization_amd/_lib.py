@@ -21,6 +21,7 @@ QL_ASCALE_DUAL, QL_ASCALE_SYMMETRIC = 0, 1
 EXPORTS = (
     "qlinear_plan", "qlinear_plan_destroy", "qlinear_plan_weights", "qlinear_quantize_act",
     "qlinear_gemm", "qlinear_cfg_combine", "qlinear_last_error", "qlinear_version",
+    "qlinear_plan_lsb_view", "qlinear_plan_lsb_update",
 )
 
 
@@ -58,6 +59,8 @@ def load() -> ctypes.CDLL:
         "qlinear_plan": ([ctypes.POINTER(QlDesc), P, P, ctypes.POINTER(P)], ctypes.c_int),
         "qlinear_plan_destroy": ([P], ctypes.c_int),
         "qlinear_plan_weights": ([P, P, P, P], ctypes.c_int),
+        "qlinear_plan_lsb_view": ([P, I32, P, ctypes.POINTER(P)], ctypes.c_int),
+        "qlinear_plan_lsb_update": ([P, P, I32, P], ctypes.c_int),
         "qlinear_quantize_act": ([P, P, I32, I32, P, P, P, P], ctypes.c_int),
         "qlinear_gemm": ([P, P, P, I32, I32, F32, P, P, P], ctypes.c_int),
         "qlinear_cfg_combine": ([P, I32, I32, F32, P, P], ctypes.c_int),

@@ -4,7 +4,9 @@
 // rotation of the weight rows (HQ-DM explainer 2.1 applied to both operands),
 // symmetric absmax scales per output channel or per output segment
 // (SegQuant explainer 2.A: each chunk of a segmented linear's output is
-// quantized on its own), round-half-even codes, 4-bit packing.
+// quantized on its own), round-half-even codes, and the weight-side LSB
+// truncation of TASQ (TASQ explainer, technical summary 2: a per-layer,
+// per-step operating precision over one stored set of codes).
 // K3 is the guided prediction of the "Closing the Null Space" explainer,
 // problem statement.
 #include "ql_device.h"
@@ -94,6 +96,31 @@ __global__ __launch_bounds__(256) void k0_quant_w(const float* W, const float* s
       ((uint32_t)(c3 & 0xFF) << 24);
 }
 
+// TASQ on the weight side: clear the k low bits of every code's magnitude,
+// sign kept (keep = ~(2^k - 1)), 16 codes per thread; the first N threads
+// also copy the weight scales, so a rewrite is one launch.
+__device__ __forceinline__ uint32_t truncate4(uint32_t v, int32_t keep) {
+  uint32_t r = 0;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int c = (int)(int8_t)((v >> (8 * i)) & 0xFFu);
+    const int t = c >= 0 ? (c & keep) : -((-c) & keep);
+    r |= ((uint32_t)t & 0xFFu) << (8 * i);
+  }
+  return r;
+}
+
+__global__ __launch_bounds__(256) void k0_truncate_w(const uint4* in, int64_t n16, int32_t keep,
+                                                     uint4* out, const float* sw_in, float* sw_out,
+                                                     int N) {
+  const int64_t u = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (u < N) sw_out[u] = sw_in[u];
+  if (u >= n16) return;
+  const uint4 v = in[u];
+  out[u] = make_uint4(truncate4(v.x, keep), truncate4(v.y, keep), truncate4(v.z, keep),
+                      truncate4(v.w, keep));
+}
+
 // K3: out = yu + w * (yc - yu); yc = Y[e], yu = Y[e + half].
 __global__ __launch_bounds__(256) void k3_cfg(const float* Y, int64_t half, float w, float* out) {
   const int64_t stride = (int64_t)gridDim.x * 256;
@@ -148,6 +175,18 @@ hipError_t launch_quantize_weights(const float* W, const float* sw, int N, int K
   const int64_t nunits = (int64_t)N * K / 4;
   hipLaunchKernelGGL(k0_quant_w, dim3(blocks_for(nunits, 256)), dim3(256), 0, s, W, sw, K, nunits,
                      qw, out);
+  return hipGetLastError();
+}
+
+hipError_t launch_truncate_weights(const uint8_t* in, int64_t nbytes, int k, uint8_t* out,
+                                   const float* sw_in, float* sw_out, int N, hipStream_t s) {
+  if (nbytes % 16 != 0 || k < 0 || k > 7) return hipErrorInvalidValue;
+  const int64_t n16 = nbytes / 16;
+  const int32_t keep = ~((1 << k) - 1);
+  const int64_t threads = n16 > N ? n16 : N;
+  hipLaunchKernelGGL(k0_truncate_w, dim3(blocks_for(threads, 256)), dim3(256), 0, s,
+                     reinterpret_cast<const uint4*>(in), n16, keep, reinterpret_cast<uint4*>(out),
+                     sw_in, sw_out, N);
   return hipGetLastError();
 }
 

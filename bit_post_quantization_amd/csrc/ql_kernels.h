@@ -59,5 +59,9 @@ hipError_t launch_weight_scales(const uint32_t* rowmax, int N, int mode, const i
                                 int nseg, float qw, float* sw, hipStream_t s);
 hipError_t launch_quantize_weights(const float* W, const float* sw, int N, int K, float qw,
                                    uint8_t* out, hipStream_t s);
+// Weight codes with the k low magnitude bits cleared (nbytes % 16 == 0,
+// 16-byte aligned), and a copy of the N weight scales.
+hipError_t launch_truncate_weights(const uint8_t* in, int64_t nbytes, int k, uint8_t* out,
+                                   const float* sw_in, float* sw_out, int N, hipStream_t s);
 
 }  // namespace ql

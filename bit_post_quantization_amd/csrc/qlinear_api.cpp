@@ -16,7 +16,7 @@ struct qlinear_plan {
   ql_desc d;
   std::vector<int32_t> seg;  // host copy, n_segments + 1
   int device = -1;
-  uint8_t* wq = nullptr;     // weight codes, int8 [N,K] or packed [N,K/2]
+  uint8_t* wq = nullptr;     // weight codes, int8 [N,K]
   float* sw = nullptr;       // weight scales [N]
   ql::ReduceWs* ws = nullptr;
 };
@@ -103,6 +103,27 @@ void free_plan(struct qlinear_plan* p) {
   if (p->sw) (void)hipFree(p->sw);
   if (p->ws) (void)hipFree(p->ws);
   delete p;
+}
+
+// Two plans with the same descriptor and segments: weights of one can stand
+// in for the other's in every call.
+bool same_layer(const struct qlinear_plan* a, const struct qlinear_plan* b) {
+  const ql_desc &x = a->d, &y = b->d;
+  return x.N == y.N && x.K == y.K && x.w_bits == y.w_bits && x.a_bits == y.a_bits &&
+         x.hadamard_block == y.hadamard_block && x.n_segments == y.n_segments &&
+         x.w_scale_mode == y.w_scale_mode && x.a_scale_mode == y.a_scale_mode &&
+         x.x_dtype == y.x_dtype && a->seg == b->seg && a->device == b->device;
+}
+
+// Enqueue view's weights = base's codes with k low magnitude bits cleared,
+// and base's scales.
+ql_status enqueue_lsb(struct qlinear_plan* view, const struct qlinear_plan* base, int k,
+                      hipStream_t s) {
+  const int64_t nbytes = (int64_t)base->d.N * base->d.K;
+  hipError_t e = ql::launch_truncate_weights(base->wq, nbytes, k, view->wq, base->sw, view->sw,
+                                             base->d.N, s);
+  if (e != hipSuccess) return hip_fail(e, "truncating weight codes");
+  return QL_OK;
 }
 
 }  // namespace
@@ -193,6 +214,57 @@ ql_status qlinear_plan(const ql_desc* d, const float* W, void* stream, qlinear_p
 
 ql_status qlinear_plan_destroy(qlinear_plan_t p) {
   free_plan(p);
+  return ok();
+}
+
+ql_status qlinear_plan_lsb_view(qlinear_plan_t base, int32_t w_lsb_k, void* stream,
+                                qlinear_plan_t* out) {
+  ql_status st = check_plan(base);
+  if (st != QL_OK) return st;
+  if (!out) return fail(QL_ERR_ARG, "out is NULL");
+  if (w_lsb_k < 0 || w_lsb_k >= base->d.w_bits)
+    return fail(QL_ERR_ARG, "w_lsb_k = %d must be in [0, %d)", w_lsb_k, base->d.w_bits);
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  auto* v = new struct qlinear_plan();
+  v->d = base->d;
+  v->seg = base->seg;
+  v->device = base->device;
+  const size_t wbytes = (size_t)base->d.N * base->d.K;
+  hipError_t e = hipMalloc(&v->wq, wbytes);
+  if (e == hipSuccess) e = hipMalloc(&v->sw, (size_t)base->d.N * sizeof(float));
+  if (e == hipSuccess) e = hipMalloc(&v->ws, sizeof(ql::ReduceWs));
+  if (e != hipSuccess) {
+    free_plan(v);
+    return hip_fail(e, "allocating view plan");
+  }
+  st = enqueue_lsb(v, base, w_lsb_k, s);
+  if (st != QL_OK) {
+    (void)hipStreamSynchronize(s);
+    free_plan(v);
+    return st;
+  }
+  e = hipStreamSynchronize(s);
+  if (e != hipSuccess) {
+    free_plan(v);
+    return hip_fail(e, "synchronising view stream");
+  }
+  *out = v;
+  return ok();
+}
+
+ql_status qlinear_plan_lsb_update(qlinear_plan_t view, qlinear_plan_t base, int32_t w_lsb_k,
+                                  void* stream) {
+  ql_status st = check_plan(base);
+  if (st != QL_OK) return st;
+  st = check_plan(view);
+  if (st != QL_OK) return st;
+  if (view == base) return fail(QL_ERR_ARG, "view and base are the same plan");
+  if (!same_layer(view, base))
+    return fail(QL_ERR_ARG, "view and base differ in descriptor or segments");
+  if (w_lsb_k < 0 || w_lsb_k >= base->d.w_bits)
+    return fail(QL_ERR_ARG, "w_lsb_k = %d must be in [0, %d)", w_lsb_k, base->d.w_bits);
+  st = enqueue_lsb(view, base, w_lsb_k, reinterpret_cast<hipStream_t>(stream));
+  if (st != QL_OK) return st;
   return ok();
 }
 

@@ -85,6 +85,18 @@ def qlinear_plan_weights(plan: Plan, w_codes, w_scales, stream=None) -> None:
                                            _stream(stream)))
 
 
+def qlinear_plan_lsb_view(base: Plan, w_lsb_k: int, stream=None) -> Plan:
+    h = ctypes.c_void_p()
+    check(_lib.load().qlinear_plan_lsb_view(base.handle, w_lsb_k, _stream(stream),
+                                            ctypes.byref(h)))
+    return Plan(h.value, dict(base.desc))
+
+
+def qlinear_plan_lsb_update(view: Plan, base: Plan, w_lsb_k: int, stream=None) -> None:
+    check(_lib.load().qlinear_plan_lsb_update(view.handle, base.handle, w_lsb_k,
+                                              _stream(stream)))
+
+
 def qlinear_quantize_act(plan: Plan, X, M: int, lsb_k: int, static_scales, codes, act_scales,
                          stream=None) -> None:
     check(_lib.load().qlinear_quantize_act(plan.handle, _ptr(X), M, lsb_k, _ptr(static_scales),
@@ -118,6 +130,19 @@ class QuantLinear:
         self.a_bits, self.w_bits = a_bits, w_bits
         self.plan = qlinear_plan(W, self.N, self.K, w_bits, a_bits, hadamard_block, seg_offsets,
                                  w_scale, a_scale, x_dtype, stream)
+        self.base = None
+
+    def lsb_view(self, w_lsb_k: int, stream=None) -> "QuantLinear":
+        """The same layer run with w_lsb_k low bits of every weight code
+        dropped; ``update_lsb`` changes the depth later without allocating."""
+        v = QuantLinear.__new__(QuantLinear)
+        v.N, v.K, v.a_bits, v.w_bits = self.N, self.K, self.a_bits, self.w_bits
+        v.plan = qlinear_plan_lsb_view(self.plan, w_lsb_k, stream)
+        v.base = self
+        return v
+
+    def update_lsb(self, w_lsb_k: int, stream=None) -> None:
+        qlinear_plan_lsb_update(self.plan, self.base.plan, w_lsb_k, stream)
 
     def code_shape(self, M: int):
         return (M, self.K if self.a_bits == 8 else self.K // 2)

@@ -118,6 +118,41 @@ ql_status qlinear_plan_destroy(qlinear_plan_t p);
 ql_status qlinear_plan_weights(qlinear_plan_t p, int8_t* w_codes, float* w_scales, void* stream);
 
 /*
+ * Weight-side operating precision of TASQ (TASQ explainer, technical summary
+ * 2, shared weights with an LSB mask): one stored set of weight codes, run
+ * at a per-layer, per-step precision by dropping low bits of every code.
+ * Reading of the mask equation there: a layer run with w_lsb_k dropped bits
+ * uses c' = sign(c) * (|c| with its w_lsb_k low bits cleared), the same
+ * truncation as lsb_k of qlinear_quantize_act, and keeps its weight scales.
+ *
+ * qlinear_plan_lsb_view: make a new plan whose weight codes are base's
+ * truncated by w_lsb_k and whose descriptor, segments and scales are base's.
+ * The view owns its memory (codes, a copy of the scales, its own reduction
+ * workspace), is destroyed with qlinear_plan_destroy in any order relative
+ * to base, and is used in every call like a plan. Allocates device memory
+ * and synchronises `stream` before it returns.
+ *   base     : plan on the current device.
+ *   w_lsb_k  : 0 <= w_lsb_k < w_bits (0 gives a copy of base).
+ *   out      : HOST; receives the view handle.
+ * Errors: QL_ERR_ARG (NULL, w_lsb_k out of range, base on another device),
+ * QL_ERR_OOM, QL_ERR_HIP.
+ */
+ql_status qlinear_plan_lsb_view(qlinear_plan_t base, int32_t w_lsb_k, void* stream,
+                                qlinear_plan_t* out);
+
+/*
+ * Rewrite the weights of an existing view for a new step: view's codes =
+ * base's truncated by w_lsb_k, view's scales = base's. Enqueued on `stream`
+ * with no allocation and no host synchronisation, so a sampler keeps one
+ * operating copy per layer and changes its precision between steps. Work
+ * already enqueued on view must be ordered before this call (same stream
+ * or events). Errors: QL_ERR_ARG (NULL, view == base, w_lsb_k out of range,
+ * view and base with different descriptors or segments), QL_ERR_HIP.
+ */
+ql_status qlinear_plan_lsb_update(qlinear_plan_t view, qlinear_plan_t base, int32_t w_lsb_k,
+                                  void* stream);
+
+/*
  * Quantize activations X [M,K] (x_dtype of the plan) to codes.
  * Steps per element: optional block rotation (as for W), then per-tensor
  * scales over all M*K rotated values: s+ = max(0, max x)/qa and

@@ -63,6 +63,7 @@ def lib() -> ctypes.CDLL:
             "orc_quant_value": [F32, F32, F32, I32],
             "orc_truncate_lsb": [I32, I32],
             "orc_quantize_act": [P, I64, P, I32, I32, P],
+            "orc_truncate_codes": [P, I64, I32, I32, P],
             "orc_pack_int4": [P, I64, I64, P],
             "orc_unpack_int4": [P, I64, I64, P],
             "orc_weight_scales": [P, I64, I64, I32, I32, I32, P, P],
@@ -133,6 +134,14 @@ def quant_value(v: float, sp: float, sn: float, bits: int) -> int:
 
 def truncate_lsb(c: int, k: int) -> int:
     return int(lib().orc_truncate_lsb(int(c), int(k)))
+
+
+def truncate_codes(codes: np.ndarray, w_bits: int, k: int) -> np.ndarray:
+    """Stored weight codes -> operating codes with k low magnitude bits dropped."""
+    c = np.ascontiguousarray(codes, dtype=np.int8)
+    out = np.empty_like(c)
+    _ck(lib().orc_truncate_codes(_p(c), c.size, w_bits, k, _p(out)), "truncate_codes")
+    return out
 
 
 def quantize_act(x: np.ndarray, s: np.ndarray, a_bits: int, lsb_k: int = 0) -> np.ndarray:
@@ -230,6 +239,13 @@ class WeightPlan:
         self.w_bits, self.B = w_bits, B
         self.scales = weight_scales(Wr, w_bits, mode, seg_offsets)
         self.codes = quantize_weight(Wr, self.scales, w_bits)
+
+    def truncated(self, k: int) -> "WeightPlan":
+        """The same layer at an operating precision with k dropped bits."""
+        v = WeightPlan.__new__(WeightPlan)
+        v.w_bits, v.B, v.scales = self.w_bits, self.B, self.scales
+        v.codes = truncate_codes(self.codes, self.w_bits, k)
+        return v
 
 
 def quantize_activations(X: np.ndarray, a_bits: int, B: int = 0, mode: str = "dual",

@@ -115,6 +115,18 @@ int32_t orc_truncate_lsb(int32_t c, int32_t k) {
   return -((-c) & keep);
 }
 
+// [TQ] 2: one stored weight buffer; the layer's precision at a stage is set
+// by how many low bits its mask drops from every stored code.
+int orc_truncate_codes(const int8_t* in, int64_t n, int32_t w_bits, int32_t k, int8_t* out) {
+  if (!valid_bits(w_bits) || k < 0 || k >= w_bits || n < 0) return ORC_EARG;
+  const int32_t qw = qmax_for_bits(w_bits);
+  for (int64_t i = 0; i < n; ++i) {
+    if (in[i] < -qw || in[i] > qw) return ORC_EARG;
+    out[i] = (int8_t)orc_truncate_lsb(in[i], k);
+  }
+  return ORC_OK;
+}
+
 int orc_quantize_act(const float* x, int64_t n, const float* s, int32_t a_bits,
                      int32_t lsb_k, int8_t* codes) {
   if (!valid_bits(a_bits) || lsb_k < 0 || lsb_k >= a_bits || n < 0) return ORC_EARG;

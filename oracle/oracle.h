@@ -67,6 +67,11 @@ int32_t orc_truncate_lsb(int32_t c, int32_t k);
 int orc_quantize_act(const float* x, int64_t n, const float* s, int32_t a_bits,
                      int32_t lsb_k, int8_t* codes);
 
+/* [TQ] 2 on the stored weights: the operating weight codes of a layer at a
+ * stage with k dropped bits, one orc_truncate_lsb per code (scales kept).
+ * Codes must lie in [-qw, qw] of w_bits; 0 <= k < w_bits. */
+int orc_truncate_codes(const int8_t* in, int64_t n, int32_t w_bits, int32_t k, int8_t* out);
+
 /* Code storage for 4-bit codes: byte j of a row holds element 2j in bits 0-3
  * and element 2j+1 in bits 4-7, each a 4-bit two's-complement value. */
 int orc_pack_int4(const int8_t* codes, int64_t rows, int64_t K, uint8_t* out);

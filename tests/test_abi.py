@@ -101,6 +101,9 @@ def test_calls_reject_null_plan():
     assert L.qlinear_quantize_act(None, 0x1000, 4, 0, None, 0x1000, 0x1000, None) == _lib.QL_ERR_ARG
     assert L.qlinear_gemm(None, 0x1000, 0x1000, 4, 0, 1.0, 0x1000, None, None) == _lib.QL_ERR_ARG
     assert L.qlinear_plan_weights(None, None, None, None) == _lib.QL_ERR_ARG
+    h = ctypes.c_void_p()
+    assert L.qlinear_plan_lsb_view(None, 1, None, ctypes.byref(h)) == _lib.QL_ERR_ARG
+    assert L.qlinear_plan_lsb_update(None, None, 1, None) == _lib.QL_ERR_ARG
     assert L.qlinear_plan_destroy(None) == _lib.QL_OK
 
 

@@ -34,24 +34,36 @@ def sample_rows(M: int, cfg: bool, n: int = 48, seed: int = 0) -> np.ndarray:
     return np.unique(np.concatenate([np.array([e for e in edges if 0 <= e < top]), rnd]))
 
 
-def check_layer(torch, X, W, *, M, K, N, w_bits=8, a_bits=8, B=0, seg=None, w_scale="channel",
-                a_scale="dual", x_dtype="f32", cfg=0, guidance=4.0, lsb_k=0,
-                static_scales=None, rows=None, tag=""):
-    """Run one quantized linear on the GPU and check every stage against the oracle.
-    rows=None checks every output row."""
-    from bit_post_quantization_amd import QuantLinear
-    say(f"[case] {tag} M={M} K={K} N={N} w{w_bits}a{a_bits} B={B} seg={seg} {w_scale} "
-        f"{a_scale} {x_dtype} cfg={cfg} k={lsb_k} static={static_scales is not None}")
-    # --- plan / weights ---
-    Wd = _dev(torch, W)
-    ql = QuantLinear(Wd, w_bits=w_bits, a_bits=a_bits, hadamard_block=B, seg_offsets=seg,
-                     w_scale=w_scale, a_scale=a_scale, x_dtype=x_dtype)
-    wp = oracle.WeightPlan(W, w_bits, B=B, mode=w_scale, seg_offsets=seg)
+def check_weights(torch, ql, wp):
     wc_g, sw_g = ql.weights()
     torch.cuda.synchronize()
     wc_g, sw_g = wc_g.cpu().numpy(), sw_g.cpu().numpy()
     assert np.array_equal(sw_g.view(np.uint32), wp.scales.view(np.uint32)), "weight scales"
     assert np.array_equal(wc_g, wp.codes), "weight codes"
+
+
+def check_layer(torch, X, W, *, M, K, N, w_bits=8, a_bits=8, B=0, seg=None, w_scale="channel",
+                a_scale="dual", x_dtype="f32", cfg=0, guidance=4.0, lsb_k=0,
+                static_scales=None, rows=None, w_lsb_k=0, tag=""):
+    """Run one quantized linear on the GPU and check every stage against the oracle.
+    rows=None checks every output row. w_lsb_k > 0 runs the layer through a
+    weight LSB view of its plan (the base plan is destroyed first)."""
+    from bit_post_quantization_amd import QuantLinear
+    say(f"[case] {tag} M={M} K={K} N={N} w{w_bits}a{a_bits} B={B} seg={seg} {w_scale} "
+        f"{a_scale} {x_dtype} cfg={cfg} k={lsb_k} wk={w_lsb_k} "
+        f"static={static_scales is not None}")
+    # --- plan / weights ---
+    Wd = _dev(torch, W)
+    ql = QuantLinear(Wd, w_bits=w_bits, a_bits=a_bits, hadamard_block=B, seg_offsets=seg,
+                     w_scale=w_scale, a_scale=a_scale, x_dtype=x_dtype)
+    wp = oracle.WeightPlan(W, w_bits, B=B, mode=w_scale, seg_offsets=seg)
+    check_weights(torch, ql, wp)
+    if w_lsb_k:
+        view = ql.lsb_view(w_lsb_k)
+        ql.plan.destroy()
+        ql = view
+        wp = wp.truncated(w_lsb_k)
+        check_weights(torch, ql, wp)
     # --- activations ---
     Xd = _dev(torch, X) if x_dtype == "f32" else _dev(torch, X.view(np.int16))
     ss = None if static_scales is None else _dev(torch, np.asarray(static_scales, np.float32))
@@ -148,6 +160,62 @@ def test_lsb_truncation(torch, lsb_k, a_bits):
     W = synth.weight_normal(2, f"lsb/W{lsb_k}{a_bits}", N, K)
     check_layer(torch, X, W, M=M, K=K, N=N, a_bits=a_bits, w_bits=a_bits, cfg=1, lsb_k=lsb_k,
                 tag=f"lsb{lsb_k}")
+
+
+@pytest.mark.parametrize("w_bits,a_bits,wk,B,a_scale,seg", [
+    (8, 8, 1, 0, "dual", None), (8, 8, 4, 0, "dual", None), (8, 8, 7, 0, "dual", None),
+    (8, 4, 3, 128, "dual", None), (4, 4, 1, 128, "dual", None), (4, 4, 3, 0, "symmetric", None),
+    (4, 8, 2, 0, "dual", [0, 10, 11, 96])])
+def test_weight_lsb_view(torch, w_bits, a_bits, wk, B, a_scale, seg):
+    M, K, N = 130, 512, 96
+    X = synth.gelu_normal(21, f"wlsb/{w_bits}{a_bits}{wk}{B}", M, K)
+    W = synth.weight_normal(21, f"wlsb/W{w_bits}{a_bits}{wk}{B}", N, K)
+    check_layer(torch, X, W, M=M, K=K, N=N, w_bits=w_bits, a_bits=a_bits, B=B, a_scale=a_scale,
+                seg=seg, w_scale="segment" if seg else "channel", cfg=1, w_lsb_k=wk,
+                tag=f"wlsb{wk}")
+
+
+def test_weight_lsb_update(torch):
+    # One view re-targeted between steps without allocation: new depth, then
+    # another layer of the same shape; depth 0 reproduces the stored layer.
+    from bit_post_quantization_amd import QLError, QuantLinear, qlinear_plan_lsb_update
+    M, K, N = 96, 256, 160
+    Ws = [synth.weight_normal(22, f"upd/W{i}", N, K) for i in range(2)]
+    qls = [QuantLinear(_dev(torch, W)) for W in Ws]
+    wps = [oracle.WeightPlan(W, 8) for W in Ws]
+    view = qls[0].lsb_view(2)
+    check_weights(torch, view, wps[0].truncated(2))
+    X = _dev(torch, synth.silu_normal(22, "upd/X", M, K))
+    codes, s = qls[0].quantize(X)
+    for li, k in [(0, 4), (1, 2), (1, 0), (0, 0)]:
+        view.base = qls[li]
+        view.update_lsb(k)
+        check_weights(torch, view, wps[li].truncated(k))
+        Yv = view.gemm(codes, s, cfg=1)
+        Yb = qls[li].gemm(codes, s, cfg=1) if k == 0 else None
+        torch.cuda.synchronize()
+        if k == 0:
+            assert torch.equal(Yv.view(torch.int32), Yb.view(torch.int32))
+        else:
+            ap, an = oracle.gemm_dual(unpack_codes(codes.cpu().numpy(), K, 8),
+                                      wps[li].truncated(k).codes)
+            y = oracle.epilogue(ap, an, s.cpu().numpy(), wps[li].scales)
+            ref = oracle.cfg_combine(y[: M // 2], y[M // 2:], 1.0)
+            assert_close(Yv.cpu().numpy(), ref, "Y view")
+    other = QuantLinear(_dev(torch, synth.weight_normal(22, "upd/W2", N, K + 32)))
+    with pytest.raises(QLError):
+        qlinear_plan_lsb_update(view.plan, other.plan, 1)
+    with pytest.raises(QLError):
+        qlinear_plan_lsb_update(view.plan, view.plan, 1)
+    with pytest.raises(QLError):
+        qlinear_plan_lsb_update(view.plan, qls[0].plan, 8)
+    with pytest.raises(QLError):
+        qls[0].lsb_view(-1)
+    w4 = QuantLinear(_dev(torch, Ws[0]), w_bits=4)
+    with pytest.raises(QLError):
+        w4.lsb_view(4)
+    with pytest.raises(QLError):
+        qlinear_plan_lsb_update(view.plan, w4.plan, 1)  # same shape, other width
 
 
 @pytest.mark.parametrize("w_scale,seg", [
@@ -331,3 +399,30 @@ def test_config5_tasq_steps(torch):
         rows = sample_rows(wl.M, True, 16, seed=t * 1000 + li)
         check_layer(torch, X, W, M=wl.M, K=L.K, N=L.N, cfg=1, guidance=L.guidance,
                     lsb_k=int(sched[t, li]), rows=rows, tag=f"c5/t{t}/{L.name}")
+
+
+@pytest.mark.timeout(900)
+def test_config6_tasq_weight_stages(torch):
+    # One stored W8 layer per linear run through a view at the stage's depth,
+    # activations at per-step static scales calibrated on a separate input
+    # (dynamic scales of the calibration batch, from the GPU, checked here).
+    from bit_post_quantization_amd import QuantLinear
+    wl = configs.WORKLOADS["c6"]
+    ws = configs.c6_w_schedule()
+    cases = [(0, 0), (0, 2), (15, 1), (30, 3), (49, 2), (49, 4 * 13 + 3)]
+    for t, li in cases:
+        L = wl.layers[li]
+        g = configs.stage_of(wl, t)
+        Xc = configs.make_calib_x(wl, L, t)
+        qc = QuantLinear(_dev(torch, np.zeros((L.N, L.K), np.float32)))
+        _, s_cal = qc.quantize(_dev(torch, Xc))
+        torch.cuda.synchronize()
+        s_cal = s_cal.cpu().numpy()
+        assert np.array_equal(s_cal.view(np.uint32), oracle.act_scales(Xc, 8).view(np.uint32))
+        del qc, Xc
+        X = configs.make_x(wl, L, step=t)
+        W = configs.make_w(wl, L)
+        rows = sample_rows(wl.M, True, 16, seed=t * 1000 + li)
+        check_layer(torch, X, W, M=wl.M, K=L.K, N=L.N, cfg=1, guidance=L.guidance,
+                    static_scales=s_cal, w_lsb_k=int(ws[g, li]), rows=rows,
+                    tag=f"c6/t{t}/g{g}/{L.name}")

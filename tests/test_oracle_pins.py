@@ -309,6 +309,47 @@ def test_lsb_properties_all_codes(orc):
                 assert t == c
 
 
+def test_weight_truncation_bit_planes(orc):
+    # A stored code with k planes masked keeps the sign and the planes >= k
+    # of its magnitude (the mask equation of TASQ read bit-plane-wise).
+    for w_bits in (8, 4):
+        q = (1 << (w_bits - 1)) - 1
+        c = np.arange(-q, q + 1, dtype=np.int8)
+        planes = np.unpackbits(np.abs(c.astype(np.int16)).astype(np.uint8)[:, None], axis=1,
+                               bitorder="little")
+        for k in range(w_bits):
+            kept = (planes[:, k:] * (1 << np.arange(k, 8))).sum(axis=1)
+            t = orc.truncate_codes(c, w_bits, k)
+            assert np.array_equal(t.astype(np.int64), np.sign(c) * kept), (w_bits, k)
+        with pytest.raises(orc.OracleError):
+            orc.truncate_codes(c, w_bits, w_bits)
+        with pytest.raises(orc.OracleError):
+            orc.truncate_codes(np.array([-(q + 1)], np.int8), w_bits, 1)
+
+
+def test_weight_truncation_gemm(orc):
+    # Dropping 4 planes of 8-bit codes leaves a 4-bit grid (codes 16 * j,
+    # |j| <= 7): the layer equals the one with codes j and scales 16 * s_w,
+    # bit for bit, since the factor 16 is exact in int32 and in fp32.
+    W = synth.weight_normal(12, "t/tq/W", 48, 64)
+    x = synth.silu_normal(12, "t/tq/X", 24, 64)
+    wp = orc.WeightPlan(W, 8)
+    v = wp.truncated(4)
+    assert np.all(v.codes % 16 == 0) and np.abs(v.codes).max() <= 112
+    s = orc.act_scales(x, 8)
+    codes = orc.quantize_act(x, s, 8)
+    y = orc.epilogue(*orc.gemm_dual(codes, v.codes), s, v.scales)
+    y16 = orc.epilogue(*orc.gemm_dual(codes, (v.codes // 16).astype(np.int8)), s,
+                       (v.scales * np.float32(16)).astype(np.float32))
+    assert np.array_equal(y.view(np.uint32), y16.view(np.uint32))
+    # The dropped planes carry the rest of the full-precision product.
+    ap, an = orc.gemm_dual(codes, wp.codes)
+    tp, tn = orc.gemm_dual(codes, v.codes)
+    rp, rn = orc.gemm_dual(codes, (wp.codes - v.codes).astype(np.int8))
+    assert np.array_equal(tp + rp, ap) and np.array_equal(tn + rn, an)
+    assert np.array_equal(wp.truncated(0).codes, wp.codes)
+
+
 def test_quantize_with_lsb(orc):
     x = synth.silu_normal(11, "t/p9", 20, 64)
     s = orc.act_scales(x, 8)

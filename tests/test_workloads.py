@@ -53,3 +53,10 @@ def test_workload_tables():
     assert len(wl["c5"].layers) == 112
     sch = configs.c5_schedule()
     assert sch.shape == (50, 112) and set(np.unique(sch).tolist()) == {0, 2, 4}
+    c6 = wl["c6"]
+    assert len(c6.layers) == 112 and c6.steps == 50 and c6.stages == 4
+    ws = configs.c6_w_schedule()
+    assert ws.shape == (4, 112) and set(np.unique(ws).tolist()) == {0, 2, 4}
+    stages = [configs.stage_of(c6, t) for t in range(c6.steps)]
+    assert stages == sorted(stages) and set(stages) == {0, 1, 2, 3}
+    assert max(stages.count(g) for g in range(4)) - min(stages.count(g) for g in range(4)) <= 1

@@ -52,6 +52,7 @@ class Workload:
     layers: Tuple[Layer, ...]
     steps: int = 1
     lsb_choices: Tuple[int, ...] = (0,)
+    stages: int = 1
     notes: str = ""
 
 
@@ -105,7 +106,35 @@ def _c5() -> Workload:
         steps=50, lsb_choices=(0, 2, 4))
 
 
-WORKLOADS = {w.key: w for w in (_c1(), _c2(), _c3(), _c4(), _c5())}
+def _c6() -> Workload:
+    return Workload(
+        key="c6", title="TASQ weight-side sweep: 28 DiT-XL/2 blocks x 4 linears, 50 steps in 4 "
+                        "stages, one stored W8 buffer per linear, weight LSB depth per (stage, "
+                        "layer) in {0,2,4}, per-step static activation scales",
+        M=4096,
+        layers=tuple(Layer(f"b{b}.{n}", k, nn, x_kind="silu", cfg=True)
+                     for b in range(28) for n, k, nn in DIT_SHAPES),
+        steps=50, lsb_choices=(0, 2, 4), stages=4)
+
+
+WORKLOADS = {w.key: w for w in (_c1(), _c2(), _c3(), _c4(), _c5(), _c6())}
+
+
+def c6_w_schedule(seed: int = SEED) -> np.ndarray:
+    """int32 [4, 112]: weight LSB depth per (stage, layer), uniform over {0,2,4}."""
+    w = WORKLOADS["c6"]
+    return synth.uniform_choice_schedule(seed, "c6/wlsb", w.stages, len(w.layers), w.lsb_choices)
+
+
+def stage_of(wl: Workload, t: int) -> int:
+    """Denoising stage of step t: the steps split into `stages` runs of
+    consecutive steps, as equal as the step count allows."""
+    return t * wl.stages // wl.steps
+
+
+def make_calib_x(wl: Workload, layer: Layer, step: int, seed: int = SEED) -> np.ndarray:
+    """Calibration input of a layer at a step, drawn apart from the run's inputs."""
+    return synth.silu_normal(seed, f"{wl.key}/calib/t{step}/{layer.name}/X", wl.M, layer.K)
 
 
 def c5_schedule(seed: int = SEED) -> np.ndarray:
