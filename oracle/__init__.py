@@ -72,6 +72,7 @@ def lib() -> ctypes.CDLL:
             "orc_epilogue": [P, P, I64, I64, P, P, I32, I32, P],
             "orc_cfg_combine": [P, P, I64, I64, F32, P],
             "orc_bf16_to_f32": [P, I64, P],
+            "orc_gamp_allocate": [I32, P, P, I32, I64, P, P],
         }
         for name, args in sigs.items():
             fn = getattr(L, name)
@@ -226,6 +227,18 @@ def cfg_combine(y_c: np.ndarray, y_u: np.ndarray, w: float) -> np.ndarray:
     out = np.empty_like(y_c)
     _ck(lib().orc_cfg_combine(_p(y_c), _p(y_u), rows, N, float(w), _p(out)), "cfg_combine")
     return out
+
+
+def gamp_allocate(macs, gain, w_bits: int, budget: int):
+    """(a_bits int32 [n], total BOPs) of the greedy A4->A8 allocation."""
+    macs = np.ascontiguousarray(macs, dtype=np.int64)
+    gain = np.ascontiguousarray(gain, dtype=np.float64)
+    assert macs.shape == gain.shape and macs.ndim == 1
+    a = np.empty(macs.size, dtype=np.int32)
+    b = np.zeros(1, dtype=np.int64)
+    _ck(lib().orc_gamp_allocate(macs.size, _p(macs), _p(gain), w_bits, int(budget), _p(a), _p(b)),
+        "gamp_allocate")
+    return a, int(b[0])
 
 
 # --------------------------------------------------------------- pipeline ----

@@ -13,6 +13,7 @@
 
 #include <cfenv>
 #include <cmath>
+#include <vector>
 #include <cstdint>
 
 namespace {
@@ -306,6 +307,43 @@ int orc_cfg_combine(const float* y_c, const float* y_u, int64_t nrows, int64_t N
     const float t = w * d;
     out[e] = y_u[e] + t;
   }
+  return ORC_OK;
+}
+
+// [CFG] methodology, allocation strategy: a greedy knapsack over layers,
+// items ranked by sensitivity per BOP, each promotion from 4 to 8 activation
+// bits costing macs * w_bits * 4 BOPs. Selection by repeated scans for the
+// best remaining item (first index wins a tie).
+int orc_gamp_allocate(int32_t n, const int64_t* macs, const double* gain, int32_t w_bits,
+                      int64_t budget, int32_t* a_bits, int64_t* bops) {
+  if (n < 1 || !valid_bits(w_bits)) return ORC_EARG;
+  int64_t total = 0;
+  for (int32_t l = 0; l < n; ++l) {
+    if (macs[l] <= 0 || !std::isfinite(gain[l]) || gain[l] < 0.0) return ORC_EARG;
+    a_bits[l] = 4;
+    total += macs[l] * w_bits * 4;
+  }
+  if (budget < total) return ORC_EARG;
+  std::vector<bool> seen(n, false);
+  for (int32_t round = 0; round < n; ++round) {
+    int32_t best = -1;
+    double best_ratio = 0.0;
+    for (int32_t l = 0; l < n; ++l) {
+      if (seen[l]) continue;
+      const double ratio = gain[l] / (double)(macs[l] * w_bits * 4);
+      if (best < 0 || ratio > best_ratio) {
+        best = l;
+        best_ratio = ratio;
+      }
+    }
+    seen[best] = true;
+    const int64_t cost = macs[best] * w_bits * 4;
+    if (total + cost <= budget) {
+      a_bits[best] = 8;
+      total += cost;
+    }
+  }
+  *bops = total;
   return ORC_OK;
 }
 

@@ -99,6 +99,18 @@ int orc_epilogue(const int32_t* accp, const int32_t* accn, int64_t nrows, int64_
 int orc_cfg_combine(const float* y_c, const float* y_u, int64_t nrows, int64_t N, float w,
                     float* out);
 
+/* [CFG] methodology (allocation strategy): weights fixed at w_bits, every
+ * layer starts at 4-bit activations, layers are ranked by sensitivity per
+ * bit operation, and promoted to 8-bit activations greedily while the
+ * guided step's BOPs stay within the budget.
+ *   macs[l]  : multiply-accumulates of layer l over the guided step (> 0)
+ *   gain[l]  : sensitivity removed by promoting layer l (finite, >= 0)
+ *   budget   : BOPs limit, >= the all-4-bit BOPs
+ * BOPs of a layer = macs * w_bits * a_bits (exact int64). Equal ratios rank
+ * by layer index. Out: a_bits[l] in {4, 8}, *bops = total BOPs. */
+int orc_gamp_allocate(int32_t n, const int64_t* macs, const double* gain, int32_t w_bits,
+                      int64_t budget, int32_t* a_bits, int64_t* bops);
+
 /* bf16 bit patterns -> fp32 (exact). */
 int orc_bf16_to_f32(const uint16_t* in, int64_t n, float* out);
 

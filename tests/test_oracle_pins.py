@@ -473,3 +473,68 @@ def test_bf16_conversion_exact(orc):
     f = orc.bf16_to_f32(b)
     assert np.array_equal(f.view(np.uint32) >> 16, b.astype(np.uint32))
     assert (np.abs(f - x) <= np.abs(x) * 2.0 ** -8).all()
+
+
+# ------------------------------------------------------------- GAMP ---------
+
+def test_gamp_golden(orc):
+    for c in _golden("gamp_greedy.json")["cases"]:
+        a, b = orc.gamp_allocate(c["macs"], c["gain"], c["w_bits"], c["budget"])
+        assert a.tolist() == c["a_bits"] and b == c["bops"], c["note"]
+
+
+def _brute_force(macs, gain, w_bits, budget):
+    n = len(macs)
+    base = sum(m * w_bits * 4 for m in macs)
+    best = 0.0
+    for mask in range(1 << n):
+        cost = base + sum(macs[l] * w_bits * 4 for l in range(n) if mask >> l & 1)
+        if cost <= budget:
+            best = max(best, sum(gain[l] for l in range(n) if mask >> l & 1))
+    return best
+
+
+def test_gamp_against_exhaustive_search(orc):
+    rng = np.random.default_rng(7)
+    for trial in range(200):
+        n = int(rng.integers(1, 9))
+        w_bits = int(rng.choice([4, 8]))
+        gain = rng.lognormal(0, 1, n)
+        equal = trial % 2 == 0
+        macs = np.full(n, 1000, np.int64) if equal else rng.integers(1, 5000, n)
+        base = int(sum(int(m) * w_bits * 4 for m in macs))
+        budget = base + int(rng.integers(0, int(macs.sum()) * w_bits * 4 + 1))
+        a, bops = orc.gamp_allocate(macs, gain, w_bits, budget)
+        assert set(a.tolist()) <= {4, 8}
+        assert bops == int(sum(int(m) * w_bits * int(b) for m, b in zip(macs, a))) <= budget
+        got = float(sum(g for g, b in zip(gain, a) if b == 8))
+        opt = _brute_force([int(m) for m in macs], list(gain), w_bits, budget)
+        if equal:
+            # equal costs: the greedy by gain is the optimum
+            assert got == pytest.approx(opt, rel=1e-12)
+        else:
+            # greedy knapsack bound: greedy + the largest single gain >= optimum
+            assert got + gain.max() >= opt * (1 - 1e-12)
+        # no unpromoted layer still fits in the remaining budget
+        for l in range(n):
+            if a[l] == 4:
+                assert bops + int(macs[l]) * w_bits * 4 > budget
+
+
+def test_gamp_extremes(orc):
+    macs = np.array([5, 7, 11, 13], np.int64)
+    gain = np.array([0.5, 3.0, 1.0, 2.0])
+    lo = int(macs.sum()) * 4 * 4
+    a, b = orc.gamp_allocate(macs, gain, 4, lo)
+    assert a.tolist() == [4, 4, 4, 4] and b == lo
+    a, b = orc.gamp_allocate(macs, gain, 4, 2 * lo)
+    assert a.tolist() == [8, 8, 8, 8] and b == 2 * lo
+    for bad in [dict(budget=lo - 1), dict(w_bits=6)]:
+        kw = dict(macs=macs, gain=gain, w_bits=4, budget=lo)
+        kw.update(bad)
+        with pytest.raises(orc.OracleError):
+            orc.gamp_allocate(**kw)
+    with pytest.raises(orc.OracleError):
+        orc.gamp_allocate(np.array([0, 1]), np.array([1.0, 1.0]), 4, 1000)
+    with pytest.raises(orc.OracleError):
+        orc.gamp_allocate(np.array([1, 1]), np.array([-1.0, 1.0]), 4, 1000)
