@@ -37,7 +37,7 @@ def parse():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=50)
     p.add_argument("--warmup", type=int, default=10)
-    p.add_argument("--workload", default="mlp", help="mlp (default) | block | c3 | c4 | c5 | c6")
+    p.add_argument("--workload", default="mlp", help="mlp (default) | block | c3 | c4 | c4g | c5 | c6")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=12.0,
                    help="approximate CPU time budget of the oracle baseline")
@@ -58,6 +58,14 @@ def layers_for(name):
     if name in ("c3", "c4"):
         wl = configs.WORKLOADS[name]
         return wl, list(wl.layers)
+    if name == "c4g":
+        # The MM-DiT stack with activation bits from the greedy allocation
+        # (library host code) instead of the seeded mask.
+        import dataclasses
+        from bit_post_quantization_amd import qlinear_gamp_allocate
+        wl, macs, gain, budget = configs.c4_gamp_inputs()
+        bits, _ = qlinear_gamp_allocate(macs.tolist(), gain.tolist(), 4, budget)
+        return wl, [dataclasses.replace(L, a_bits=b) for L, b in zip(wl.layers, bits)]
     raise SystemExit(f"unknown workload {name}")
 
 
@@ -94,6 +102,20 @@ class Layer:
         from bit_post_quantization_amd import qlinear_gemm
         qlinear_gemm(self.ql.plan, self.codes, self.scales, self.M, int(self.L.cfg),
                      self.L.guidance, self.Y)
+
+
+def bops_report(Ls, M):
+    """Bit operations (MACs x w_bits x a_bits) of one guided step, both CFG
+    halves, as the guidance-aware page asks, beside the single-pass count
+    that standard metrics report and the uniform W4A8 / W4A4 stacks."""
+    macs = [M * L.N * L.K for L in Ls]
+    guided = sum(m * L.w_bits * L.a_bits for m, L in zip(macs, Ls))
+    w4a8 = sum(m * 4 * 8 for m in macs)
+    w4a4 = sum(m * 4 * 4 for m in macs)
+    return {"a_bits": [L.a_bits for L in Ls], "guided_step": guided,
+            "single_pass": guided // 2, "uniform_w4a8": w4a8, "uniform_w4a4": w4a4,
+            "vs_w4a8": round(guided / w4a8, 4),
+            "mean_a_bits_by_macs": round(guided / (4 * sum(macs)), 3)}
 
 
 def cpu_baseline(layers, budget_s):
@@ -457,7 +479,9 @@ def main():
             "workload": {"mlp": "DiT-XL/2 MLP fc1 1152->4608 + fc2 4608->1152",
                          "block": "DiT-XL/2 block QKV+proj+fc1+fc2",
                          "c3": "DiT-XL/2 block W4A4 + Hadamard-128",
-                         "c4": "MM-DiT SegLinear layers W4 A4/A8"}[args.workload],
+                         "c4": "MM-DiT SegLinear layers W4 A4/A8",
+                         "c4g": "MM-DiT SegLinear layers W4, A4/A8 by the greedy allocation"
+                         }[args.workload],
             "M": wl.M, "images": 16, "tokens_per_image": 256, "cfg_guidance": first.guidance,
             "w_bits": first.w_bits, "a_bits": first.a_bits, "act_scales": first.a_scale,
             "weight_scales": first.w_scale, "hadamard_block": first.hadamard_block,
@@ -479,6 +503,8 @@ def main():
         "layers": per_layer,
         "wall_s": round(wall, 3),
     }
+    if args.workload in ("c4", "c4g"):
+        out["bops"] = bops_report(Ls, wl.M)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(layers, args.cpu_seconds)
     print(json.dumps(out), flush=True)

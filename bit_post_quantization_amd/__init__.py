@@ -8,7 +8,8 @@ an fp32 epilogue with the classifier-free-guidance combine -- all in hand-writte
 HIP kernels for gfx950 behind the C ABI of include/qlinear.h.
 """
 from .qlinear import (  # noqa: F401
-    Plan, QLError, QuantLinear, qlinear_cfg_combine, qlinear_gemm, qlinear_plan,
+    Plan, QLError, QuantLinear, qlinear_cfg_combine, qlinear_gamp_allocate, qlinear_gemm,
+    qlinear_plan,
     qlinear_plan_destroy, qlinear_plan_lsb_update, qlinear_plan_lsb_view, qlinear_plan_weights,
     qlinear_quantize_act, qlinear_version,
 )

@@ -21,7 +21,7 @@ QL_ASCALE_DUAL, QL_ASCALE_SYMMETRIC = 0, 1
 EXPORTS = (
     "qlinear_plan", "qlinear_plan_destroy", "qlinear_plan_weights", "qlinear_quantize_act",
     "qlinear_gemm", "qlinear_cfg_combine", "qlinear_last_error", "qlinear_version",
-    "qlinear_plan_lsb_view", "qlinear_plan_lsb_update",
+    "qlinear_plan_lsb_view", "qlinear_plan_lsb_update", "qlinear_gamp_allocate",
 )
 
 
@@ -61,6 +61,7 @@ def load() -> ctypes.CDLL:
         "qlinear_plan_weights": ([P, P, P, P], ctypes.c_int),
         "qlinear_plan_lsb_view": ([P, I32, P, ctypes.POINTER(P)], ctypes.c_int),
         "qlinear_plan_lsb_update": ([P, P, I32, P], ctypes.c_int),
+        "qlinear_gamp_allocate": ([I32, P, P, I32, ctypes.c_int64, P, P], ctypes.c_int),
         "qlinear_quantize_act": ([P, P, I32, I32, P, P, P, P], ctypes.c_int),
         "qlinear_gemm": ([P, P, P, I32, I32, F32, P, P, P], ctypes.c_int),
         "qlinear_cfg_combine": ([P, I32, I32, F32, P, P], ctypes.c_int),

@@ -128,6 +128,14 @@ ql_status enqueue_lsb(struct qlinear_plan* view, const struct qlinear_plan* base
 
 }  // namespace
 
+namespace ql {
+// Status reporting for the host-only entry points in other files.
+ql_status set_error(ql_status st, const char* msg) {
+  if (st == QL_OK) return ok();
+  return fail(st, "%s", msg);
+}
+}  // namespace ql
+
 extern "C" {
 
 const char* qlinear_last_error(void) { return g_err.c_str(); }

@@ -113,6 +113,18 @@ def qlinear_cfg_combine(Y, M: int, N: int, w: float, out, stream=None) -> None:
     check(_lib.load().qlinear_cfg_combine(_ptr(Y), M, N, float(w), _ptr(out), _stream(stream)))
 
 
+def qlinear_gamp_allocate(macs, gain, w_bits: int, budget_bops: int):
+    """Host-only: (a_bits list, total BOPs) of the greedy A4->A8 allocation."""
+    n = len(macs)
+    m = (ctypes.c_int64 * n)(*[int(v) for v in macs])
+    g = (ctypes.c_double * n)(*[float(v) for v in gain])
+    a = (ctypes.c_int32 * n)()
+    b = ctypes.c_int64(0)
+    check(_lib.load().qlinear_gamp_allocate(n, m, g, w_bits, int(budget_bops), a,
+                                            ctypes.byref(b)))
+    return list(a), int(b.value)
+
+
 def qlinear_version() -> str:
     return _lib.load().qlinear_version().decode()
 

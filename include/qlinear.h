@@ -214,6 +214,33 @@ const char* qlinear_last_error(void);
 /* Library version string. */
 const char* qlinear_version(void);
 
+/*
+ * Host-only (no device work, usable without a GPU): GAMP's activation-bit
+ * allocation -- "Closing the Null Space" explainer, methodology (allocation
+ * strategy), with BOPs counted over the guided step as its key contribution
+ * 4 asks. Weights stay at w_bits; every layer starts at 4-bit activations;
+ * layers are ranked by gain[l] / (macs[l] * w_bits * 4), the sensitivity
+ * removed per bit operation added by a promotion (equal ratios keep layer
+ * order), and promoted to 8-bit activations in that order whenever the
+ * total still fits the budget (a layer that does not fit is skipped and the
+ * scan goes on).
+ *   n_layers    : >= 1.
+ *   macs        : HOST int64 [n_layers], multiply-accumulates of each layer
+ *                 over the guided step (both CFG branches), in [1, 2^52].
+ *   gain        : HOST double [n_layers], finite, >= 0: the guided-output
+ *                 error removed by running layer l at 8 instead of 4 bits.
+ *   w_bits      : 4 or 8.
+ *   budget_bops : total BOPs allowed, sum of macs * w_bits * a_bits; at
+ *                 least the all-4-bit total.
+ *   a_bits      : HOST out int32 [n_layers], 4 or 8.
+ *   bops        : HOST out, the allocation's total BOPs (exact).
+ * Errors: QL_ERR_ARG (NULL, bad sizes or values, budget below the all-4-bit
+ * total, totals beyond int64).
+ */
+ql_status qlinear_gamp_allocate(int32_t n_layers, const int64_t* macs, const double* gain,
+                                int32_t w_bits, int64_t budget_bops, int32_t* a_bits,
+                                int64_t* bops);
+
 #ifdef __cplusplus
 }
 #endif

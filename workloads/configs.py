@@ -126,6 +126,18 @@ def c6_w_schedule(seed: int = SEED) -> np.ndarray:
     return synth.uniform_choice_schedule(seed, "c6/wlsb", w.stages, len(w.layers), w.lsb_choices)
 
 
+def c4_gamp_inputs(seed: int = SEED):
+    """Inputs of the activation-bit allocation for the MM-DiT stack: per-layer
+    MACs of the whole step (M rows, both CFG halves), seeded synthetic
+    sensitivities (log-normal, one per layer), and a budget of 6 activation
+    bits on average by MACs at 4-bit weights."""
+    wl = WORKLOADS["c4"]
+    macs = np.array([wl.M * L.N * L.K for L in wl.layers], np.int64)
+    gain = synth.lognormal(seed, "c4/gamp/gain", len(wl.layers))
+    budget = int(macs.sum()) * 4 * 6
+    return wl, macs, gain, budget
+
+
 def stage_of(wl: Workload, t: int) -> int:
     """Denoising stage of step t: the steps split into `stages` runs of
     consecutive steps, as equal as the step count allows."""

@@ -74,6 +74,11 @@ def weight_normal(seed: int, name: str, N: int, K: int, std: float = 0.02) -> np
     return (std * normal_f64(seed, name, (N, K))).astype(np.float32)
 
 
+def lognormal(seed: int, name: str, n: int) -> np.ndarray:
+    """float64 [n] = exp(N(0,1)), e.g. synthetic per-layer sensitivities."""
+    return np.exp(normal_f64(seed, name, (n,)))
+
+
 def uniform_choice_schedule(seed: int, name: str, rows: int, cols: int, choices) -> np.ndarray:
     """int32 [rows, cols] drawn uniformly from `choices` (seeded)."""
     ch = np.asarray(choices, dtype=np.int32)
