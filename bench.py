@@ -104,6 +104,23 @@ class Layer:
                      self.L.guidance, self.Y)
 
 
+DATA = {
+    "gelu_outliers": "synthetic (seeded GELU(N(0,1)) activations with 0.1% x20 outlier channels, "
+                     "N(0,0.02) weights)",
+    "bf16_normal": "synthetic (seeded bf16(N(0,1)) activations, N(0,0.02) weights)",
+    "silu": "synthetic (seeded SiLU(N(0,1)) activations, N(0,0.02) weights)",
+}
+SHAPE = {
+    "c2": {"images": 16, "tokens_per_image": 256},
+    "c3": {"images": 16, "tokens_per_image": 256},
+    "c4": {"images": 4, "tokens_per_image": 4608},
+}
+
+
+def per_layer_or_one(vals):
+    return vals[0] if len(set(vals)) == 1 else vals
+
+
 def bops_report(Ls, M):
     """Bit operations (MACs x w_bits x a_bits) of one guided step, both CFG
     halves, as the guidance-aware page asks, beside the single-pass count
@@ -474,7 +491,7 @@ def main():
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "int8",
-        "data": "synthetic (seeded GELU(N(0,1)) activations with 0.1% x20 outlier channels, N(0,0.02) weights)",
+        "data": DATA[first.x_kind],
         "config": {
             "workload": {"mlp": "DiT-XL/2 MLP fc1 1152->4608 + fc2 4608->1152",
                          "block": "DiT-XL/2 block QKV+proj+fc1+fc2",
@@ -482,16 +499,18 @@ def main():
                          "c4": "MM-DiT SegLinear layers W4 A4/A8",
                          "c4g": "MM-DiT SegLinear layers W4, A4/A8 by the greedy allocation"
                          }[args.workload],
-            "M": wl.M, "images": 16, "tokens_per_image": 256, "cfg_guidance": first.guidance,
-            "w_bits": first.w_bits, "a_bits": first.a_bits, "act_scales": first.a_scale,
-            "weight_scales": first.w_scale, "hadamard_block": first.hadamard_block,
+            "M": wl.M, **SHAPE[wl.key], "cfg_guidance": first.guidance if first.cfg else None,
+            "w_bits": first.w_bits, "a_bits": per_layer_or_one([L.a_bits for L in Ls]),
+            "act_scales": first.a_scale,
+            "weight_scales": per_layer_or_one([L.w_scale for L in Ls]),
+            "hadamard_block": first.hadamard_block,
         },
         "roofline": {
             "kernel": "k2_gemm (int8 MFMA, both polarity planes, fused epilogue)",
             "bound": "mfma", "achieved": round(gemm_tops, 1), "peak": PEAK_INT8_TOPS,
             "unit": "TOPS", "frac": round(gemm_tops / PEAK_INT8_TOPS, 4),
             "ops_per_launch": ops_per_launch, "avg_launch_us": round(gemm_avg_s * 1e6, 2),
-            "traffic": measured_traffic(),
+            "traffic": measured_traffic() if args.workload == "mlp" else None,
         },
         "act_quant": {
             "kernels": "k1_reduce + k1_quantize", "bound": "hbm",

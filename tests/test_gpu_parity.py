@@ -386,6 +386,24 @@ def test_config4_mmdit_segments(torch, li):
 
 
 @pytest.mark.timeout(900)
+@pytest.mark.parametrize("li", range(4))
+def test_config4_gamp_bits(torch, li):
+    # The MM-DiT stack with activation bits from the greedy allocation.
+    import dataclasses
+    from bit_post_quantization_amd import qlinear_gamp_allocate
+    wl, macs, gain, budget = configs.c4_gamp_inputs()
+    bits, _ = qlinear_gamp_allocate(macs.tolist(), gain.tolist(), 4, budget)
+    L = dataclasses.replace(wl.layers[li], a_bits=bits[li])
+    X = configs.make_x(wl, L)
+    W = configs.make_w(wl, L)
+    rows = sample_rows(wl.M, False, 24, seed=100 + li)
+    seg = L.seg_offsets()
+    check_layer(torch, X, W, M=wl.M, K=L.K, N=L.N, w_bits=L.w_bits, a_bits=L.a_bits,
+                seg=None if seg is None else seg.tolist(), w_scale=L.w_scale,
+                x_dtype=L.x_dtype, rows=rows, tag=f"c4g/{L.name}/a{L.a_bits}")
+
+
+@pytest.mark.timeout(900)
 def test_config5_tasq_steps(torch):
     # Every layer of one block over several steps of the schedule, plus the
     # first layer of every block at step 0 (the full sweep is a benchmark).
