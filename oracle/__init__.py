@@ -73,6 +73,9 @@ def lib() -> ctypes.CDLL:
             "orc_cfg_combine": [P, P, I64, I64, F32, P],
             "orc_bf16_to_f32": [P, I64, P],
             "orc_gamp_allocate": [I32, P, P, I32, I64, P, P],
+            "orc_hadamard_weight_int": [P, I64, I64, I32, P],
+            "orc_gemm_int64": [P, P, P, I64, I64, I64, P],
+            "orc_epilogue_single": [P, I64, I64, F32, P, I32, P],
         }
         for name, args in sigs.items():
             fn = getattr(L, name)
@@ -227,6 +230,57 @@ def cfg_combine(y_c: np.ndarray, y_u: np.ndarray, w: float) -> np.ndarray:
     out = np.empty_like(y_c)
     _ck(lib().orc_cfg_combine(_p(y_c), _p(y_u), rows, N, float(w), _p(out)), "cfg_combine")
     return out
+
+
+def hadamard_weight_int(wc: np.ndarray, B: int) -> np.ndarray:
+    """int32 [N,K] = H W_int^T laid out as rows (single-Hadamard weights)."""
+    wc = np.ascontiguousarray(wc, dtype=np.int8)
+    N, K = wc.shape
+    v = np.empty((N, K), dtype=np.int32)
+    _ck(lib().orc_hadamard_weight_int(_p(wc), N, K, B, _p(v)), "hadamard_weight_int")
+    return v
+
+
+def gemm_int64(codes: np.ndarray, v: np.ndarray, rows: Optional[Sequence[int]] = None):
+    codes = np.ascontiguousarray(codes, dtype=np.int8)
+    v = np.ascontiguousarray(v, dtype=np.int32)
+    M, K = codes.shape
+    N = v.shape[0]
+    assert v.shape[1] == K
+    r = np.arange(M, dtype=np.int64) if rows is None else np.ascontiguousarray(rows, dtype=np.int64)
+    acc = np.empty((r.size, N), dtype=np.int64)
+    _ck(lib().orc_gemm_int64(_p(codes), _p(v), _p(r), r.size, N, K, _p(acc)), "gemm_int64")
+    return acc
+
+
+def epilogue_single(acc: np.ndarray, s: float, sw: np.ndarray, B: int) -> np.ndarray:
+    acc = np.ascontiguousarray(acc, dtype=np.int64)
+    sw = np.ascontiguousarray(sw, dtype=np.float32)
+    rows, N = acc.shape
+    y = np.empty((rows, N), dtype=np.float32)
+    _ck(lib().orc_epilogue_single(_p(acc), rows, N, float(s), _p(sw), B, _p(y)),
+        "epilogue_single")
+    return y
+
+
+class SingleHadamardPlan:
+    """[HQ] 2.1 single transform: W quantized unrotated (per channel /
+    segment / tensor), its codes kept, and the integer weights H W_int^T."""
+
+    def __init__(self, W: np.ndarray, w_bits: int, B: int, mode: str = "channel",
+                 seg_offsets: Optional[Sequence[int]] = None):
+        self.w_bits, self.B = w_bits, B
+        W = np.ascontiguousarray(W, dtype=np.float32)
+        self.scales = weight_scales(W, w_bits, mode, seg_offsets)
+        self.codes = quantize_weight(W, self.scales, w_bits)
+        self.v = hadamard_weight_int(self.codes, B)
+
+    def truncated(self, k: int) -> "SingleHadamardPlan":
+        p = SingleHadamardPlan.__new__(SingleHadamardPlan)
+        p.w_bits, p.B, p.scales = self.w_bits, self.B, self.scales
+        p.codes = truncate_codes(self.codes, self.w_bits, k)
+        p.v = hadamard_weight_int(p.codes, self.B)
+        return p
 
 
 def gamp_allocate(macs, gain, w_bits: int, budget: int):

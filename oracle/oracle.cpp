@@ -310,6 +310,50 @@ int orc_cfg_combine(const float* y_c, const float* y_u, int64_t nrows, int64_t N
   return ORC_OK;
 }
 
+// [HQ] 2.1, single transform: X W^T = (1/B) (X H)(H W^T) since H H = B I.
+// The weight side is kept as the integer matrix H W_int^T, from the entries
+// of the Sylvester matrix directly (no fast transform).
+int orc_hadamard_weight_int(const int8_t* wc, int64_t N, int64_t K, int32_t B, int32_t* v) {
+  if (!is_pow2(B) || K % B != 0 || N < 0) return ORC_EARG;
+  for (int64_t n = 0; n < N; ++n)
+    for (int64_t k = 0; k < K; ++k) {
+      const int64_t blk = k - k % B;
+      int64_t sum = 0;
+      for (int32_t j = 0; j < B; ++j) {
+        const int sign = (__builtin_popcount((unsigned)((k % B) & j)) & 1) ? -1 : 1;
+        sum += sign * (int64_t)wc[n * K + blk + j];
+      }
+      v[n * K + k] = (int32_t)sum;
+    }
+  return ORC_OK;
+}
+
+int orc_gemm_int64(const int8_t* c, const int32_t* v, const int64_t* rows, int64_t nrows,
+                   int64_t N, int64_t K, int64_t* acc) {
+  if (nrows < 0 || N < 0 || K < 0) return ORC_EARG;
+  for (int64_t i = 0; i < nrows; ++i)
+    for (int64_t n = 0; n < N; ++n) {
+      int64_t sum = 0;
+      for (int64_t k = 0; k < K; ++k) sum += (int64_t)c[rows[i] * K + k] * (int64_t)v[n * K + k];
+      acc[i * N + n] = sum;
+    }
+  return ORC_OK;
+}
+
+int orc_epilogue_single(const int64_t* acc, int64_t nrows, int64_t N, float s, const float* sw,
+                        int32_t B, float* y) {
+  if (nrows < 0 || N <= 0 || !is_pow2(B)) return ORC_EARG;
+  const float inv_b = 1.0f / (float)B;
+  for (int64_t i = 0; i < nrows; ++i)
+    for (int64_t n = 0; n < N; ++n) {
+      const float a = (float)acc[i * N + n];
+      const float t = a * s;
+      const float u = t * sw[n];
+      y[i * N + n] = u * inv_b;
+    }
+  return ORC_OK;
+}
+
 // [CFG] methodology, allocation strategy: a greedy knapsack over layers,
 // items ranked by sensitivity per BOP, each promotion from 4 to 8 activation
 // bits costing macs * w_bits * 4 BOPs. Selection by repeated scans for the

@@ -99,6 +99,22 @@ int orc_epilogue(const int32_t* accp, const int32_t* accn, int64_t nrows, int64_
 int orc_cfg_combine(const float* y_c, const float* y_u, int64_t nrows, int64_t N, float w,
                     float* out);
 
+/* [HQ] 2.1 single Hadamard: only the activations are rotated, so the
+ * weights enter as H * W_int^T. v[n,k] = sum over k' in the B-block of k of
+ * H[k mod B][k' mod B] * wc[n,k'], with H[i][j] = (-1)^popcount(i & j)
+ * written out entry by entry (exact integers). */
+int orc_hadamard_weight_int(const int8_t* wc, int64_t N, int64_t K, int32_t B, int32_t* v);
+
+/* Exact int64 contraction of activation codes c [*, K] (rows listed) with
+ * integer weights v [N, K]: acc[i,n] = sum_k c[row_i,k] * v[n,k]. */
+int orc_gemm_int64(const int8_t* c, const int32_t* v, const int64_t* rows, int64_t nrows,
+                   int64_t N, int64_t K, int64_t* acc);
+
+/* [HQ] 2.1 + 2.2 (symmetric activations): y = fl(fl(fl(a * s) * sw[n]) * (1/B))
+ * with a = acc rounded once to fp32 (nearest even). */
+int orc_epilogue_single(const int64_t* acc, int64_t nrows, int64_t N, float s, const float* sw,
+                        int32_t B, float* y);
+
 /* [CFG] methodology (allocation strategy): weights fixed at w_bits, every
  * layer starts at 4-bit activations, layers are ranked by sensitivity per
  * bit operation, and promoted to 8-bit activations greedily while the

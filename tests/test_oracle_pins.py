@@ -538,3 +538,70 @@ def test_gamp_extremes(orc):
         orc.gamp_allocate(np.array([0, 1]), np.array([1.0, 1.0]), 4, 1000)
     with pytest.raises(orc.OracleError):
         orc.gamp_allocate(np.array([1, 1]), np.array([-1.0, 1.0]), 4, 1000)
+
+
+# ------------------------------------------------ single Hadamard (HQ-DM) ----
+
+@pytest.mark.parametrize("B", [4, 16, 128])
+def test_single_hadamard_weights_vs_scipy(orc, B):
+    rng = np.random.default_rng(B)
+    K = 2 * B
+    wc = rng.integers(-127, 128, (5, K)).astype(np.int8)
+    v = orc.hadamard_weight_int(wc, B)
+    H = scipy.linalg.hadamard(B).astype(np.int64)
+    ref = np.concatenate([wc[:, j:j + B].astype(np.int64) @ H for j in range(0, K, B)], axis=1)
+    assert np.array_equal(v, ref)
+    # applying H again gives B times the codes (H H = B I)
+    back = np.concatenate([v[:, j:j + B].astype(np.int64) @ H for j in range(0, K, B)], axis=1)
+    assert np.array_equal(back, B * wc.astype(np.int64))
+    assert np.abs(v).max() <= B * 127
+
+
+def test_int64_gemm_beyond_int32(orc):
+    rng = np.random.default_rng(3)
+    K = 4608
+    c = np.full((2, K), 127, np.int8)
+    c[1] = rng.integers(-127, 128, K)
+    v = np.full((3, K), 16256, np.int32)
+    v[2] = rng.integers(-16256, 16257, K)
+    acc = orc.gemm_int64(c, v)
+    assert acc[0, 0] == 127 * 16256 * K > 2 ** 31
+    assert np.array_equal(acc, c.astype(np.int64) @ v.astype(np.int64).T)
+
+
+def test_single_epilogue_rounding(orc):
+    acc = np.array([[2 ** 24 + 1, 2 ** 24 + 3, -(2 ** 33 + 5), 7, 0, 123456789012]], np.int64)
+    sw = np.ones(acc.shape[1], np.float32)
+    y = orc.epilogue_single(acc, 1.0, sw, 1)
+    assert np.array_equal(y, acc.astype(np.float32))  # one round to nearest even
+    y8 = orc.epilogue_single(acc, 1.0, sw, 8)
+    assert np.array_equal(y8, acc.astype(np.float32) / np.float32(8))
+
+
+def test_single_hadamard_exact_on_grid(orc):
+    # Inputs built so that nothing is lost to quantization: X = (s/B) C H with
+    # max|C| = 127 in every tensor, W = s_w W_int with max|W_int| = 127 per
+    # row, s and s_w powers of two. The single-Hadamard layer then returns
+    # X W^T rounded once, computed here from the integers alone.
+    rng = np.random.default_rng(5)
+    B, M, K, N = 16, 6, 64, 10
+    H = scipy.linalg.hadamard(B).astype(np.int64)
+    C = rng.integers(-127, 128, (M, K))
+    C[0, 0] = 127
+    Hk = np.kron(np.eye(K // B, dtype=np.int64), H)
+    s = 2.0 ** -6
+    X = (s / B * (C @ Hk)).astype(np.float32)
+    assert np.array_equal(X.astype(np.float64), s / B * (C @ Hk))  # exact in fp32
+    Wi = rng.integers(-127, 128, (N, K))
+    Wi[:, 0] = 127
+    sw = 2.0 ** -9
+    W = (sw * Wi).astype(np.float32)
+    codes, sc = orc.quantize_activations(X, 8, B=B, mode="symmetric")
+    assert sc[0] == np.float32(s) and np.array_equal(codes, C)
+    wp = orc.SingleHadamardPlan(W, 8, B)
+    assert np.array_equal(wp.codes, Wi) and np.all(wp.scales == np.float32(sw))
+    y = orc.epilogue_single(orc.gemm_int64(codes, wp.v), sc[0], wp.scales, B)
+    exact = (C @ Hk) @ Wi.T  # = B (X W^T) / (s s_w), integers
+    ref = (exact.astype(np.float64) * (s * sw / B)).astype(np.float32)
+    assert np.array_equal(y, ref)
+    assert np.allclose(y, X.astype(np.float64) @ W.astype(np.float64).T, rtol=0, atol=1e-6)
