@@ -32,7 +32,7 @@ class QlDesc(ctypes.Structure):
         ("hadamard_block", ctypes.c_int32), ("n_segments", ctypes.c_int32),
         ("seg_offsets", ctypes.POINTER(ctypes.c_int32)),
         ("w_scale_mode", ctypes.c_int), ("a_scale_mode", ctypes.c_int),
-        ("x_dtype", ctypes.c_int),
+        ("x_dtype", ctypes.c_int), ("single_hadamard", ctypes.c_int32),
     ]
 
 

@@ -302,7 +302,7 @@ __device__ __forceinline__ void schedule_step() {
 // pair w + 8, so a step's body has no branches and every step issues the
 // same number of loads: the compiler can then prove from the explicit
 // waits below that each LDS read finds its data landed.
-template <bool A4, bool SYM, bool CFG, int NB, int CG, bool TW>
+template <bool A4, bool SYM, bool CFG, bool HS, int NB, int CG, bool TW>
 __device__ __forceinline__ void gemm_wave(const GemmArgs& g, int wave, int lane, uint8_t* st0,
                                           uint8_t* st1, uint8_t* st2, uint8_t* st3) {
   using Lay = Layout<A4, NB>;
@@ -502,6 +502,83 @@ __device__ __forceinline__ void gemm_wave(const GemmArgs& g, int wave, int lane,
   // stores (rows past the end and columns past N are dropped by the range
   // check), so no store waits on another and there are no per-element
   // branches.
+  // Single Hadamard: fragments (J0 + 2p, J0 + 2p + 1) hold the hi and lo
+  // planes of the same 16 output channels; the exact sum 128 * hi + lo is
+  // formed in fp64 (|sum| < 2^53) and rounded once to fp32.
+  auto epilogue_hs = [&](int ti) __attribute__((always_inline)) {
+    static_assert(!HS || (SYM && NBW % 2 == 0 && J0 % 2 == 0), "hi/lo fragment pairs");
+    constexpr int NPR = NBW / 2;
+    int m0, n0;
+    coords(ti, m0, n0);
+    float sw[NPR];
+    unsigned coff[NPR];
+#pragma unroll
+    for (int p = 0; p < NPR; ++p) {
+      const int col = n0 / 2 + 8 * J0 + 16 * p + i16;
+      sw[p] = g.w_scales[min(col, g.Nout - 1)];
+      coff[p] = col < g.Nout ? 4u * (unsigned)col : kOOB;
+    }
+#pragma unroll
+    for (int p = 0; p < NPR; ++p) asm volatile("" ::"v"(sw[p]));
+    const int rows_here = min(RPT, (CFG ? g.Mh : g.M) - m0);
+    const __amdgpu_buffer_rsrc_t ry =
+        make_rsrc(g.Y + (int64_t)m0 * g.Nout, (uint32_t)rows_here * (uint32_t)g.Nout * 4u);
+    const unsigned rowb = (unsigned)g.Nout * 4u;
+    auto value = [&](int fi, int p, int r) __attribute__((always_inline)) {
+      const int hi = acc[0][fi][2 * p][r] >> SHIFT;
+      const int lo = acc[0][fi][2 * p + 1][r] >> SHIFT;
+      const double e = __dadd_rn(__dmul_rn((double)hi, 128.0), (double)lo);
+      const float a = __double2float_rn(e);
+      return __fmul_rn(a, sp);
+    };
+    auto out = [&](float a, int p) __attribute__((always_inline)) {
+      return __fmul_rn(__fmul_rn(a, sw[p]), g.inv_b);
+    };
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      if constexpr (CFG) {
+        const unsigned ro = (unsigned)(16 * band + rsub + r) * rowb;
+#pragma unroll
+        for (int p = 0; p < NPR; ++p) {
+          const float yc = out(value(0, p, r), p);
+          const float yu = out(value(1, p, r), p);
+          const float d = __fsub_rn(yc, yu);
+          const float t = __fmul_rn(g.guidance, d);
+          __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(__fadd_rn(yu, t)), ry,
+                                                ro + coff[p], 0, 0);
+        }
+      } else {
+#pragma unroll
+        for (int fi = 0; fi < 2; ++fi) {
+          const unsigned ro = (unsigned)(16 * (2 * band + fi) + rsub + r) * rowb;
+#pragma unroll
+          for (int p = 0; p < NPR; ++p)
+            __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(out(value(fi, p, r), p)), ry,
+                                                  ro + coff[p], 0, 0);
+        }
+      }
+    }
+    if (g.dbg) {  // accumulator dump (testing aid): hi and lo plane sums
+      const int64_t plane = (int64_t)g.M * g.Nout;
+#pragma unroll
+      for (int fi = 0; fi < 2; ++fi)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          bool ok;
+          const int grow = a_row(m0, 2 * band + fi, rsub + r, ok);
+          if (!ok) continue;
+#pragma unroll
+          for (int p = 0; p < NPR; ++p) {
+            if (coff[p] == kOOB) continue;
+            const int64_t e = (int64_t)grow * g.Nout + (coff[p] >> 2);
+            g.dbg[e] = acc[0][fi][2 * p][r] >> SHIFT;
+            g.dbg[plane + e] = acc[0][fi][2 * p + 1][r] >> SHIFT;
+          }
+        }
+    }
+    wait_vmcnt<0>();
+  };
+
   auto epilogue = [&](int ti) __attribute__((always_inline)) {
     int m0, n0;
     coords(ti, m0, n0);
@@ -610,7 +687,10 @@ __device__ __forceinline__ void gemm_wave(const GemmArgs& g, int wave, int lane,
   // buffers are static.
   auto step_epi = [&](int s, auto uc) __attribute__((always_inline)) {
     if (step(s, uc)) {
-      epilogue(cmp_ti);
+      if constexpr (HS)
+        epilogue_hs(cmp_ti);
+      else
+        epilogue(cmp_ti);
       zero_acc();
       cmp_k = 0;
       ++cmp_ti;
@@ -628,7 +708,7 @@ __device__ __forceinline__ void gemm_wave(const GemmArgs& g, int wave, int lane,
   if (sb + 2 < total) step_epi(sb + 2, IC<2>{});
 }
 
-template <bool A4, bool SYM, bool CFG, int NB>
+template <bool A4, bool SYM, bool CFG, bool HS, int NB>
 __global__ __launch_bounds__(kThreads, 1) void k2_gemm(GemmArgs g) {
   using Lay = Layout<A4, NB>;
   // One LDS object per ring stage: the compiler tracks DMA -> LDS writes per
@@ -643,16 +723,16 @@ __global__ __launch_bounds__(kThreads, 1) void k2_gemm(GemmArgs g) {
   // waves w < NB - 8 also move weight pair w + 8 (NB is 8 or 9)
   static_assert(NB == 8 || NB == 9, "wave roles");
   if (wave < NB - 8)
-    gemm_wave<A4, SYM, CFG, NB, 0, true>(g, wave, lane, st0, st1, st2, st3);
+    gemm_wave<A4, SYM, CFG, HS, NB, 0, true>(g, wave, lane, st0, st1, st2, st3);
   else if (wave < 4)
-    gemm_wave<A4, SYM, CFG, NB, 0, false>(g, wave, lane, st0, st1, st2, st3);
+    gemm_wave<A4, SYM, CFG, HS, NB, 0, false>(g, wave, lane, st0, st1, st2, st3);
   else
-    gemm_wave<A4, SYM, CFG, NB, 1, false>(g, wave, lane, st0, st1, st2, st3);
+    gemm_wave<A4, SYM, CFG, HS, NB, 1, false>(g, wave, lane, st0, st1, st2, st3);
 }
 
 int g_cus = 0;  // compute units of the device (queried on first launch)
 
-template <bool A4, bool SYM, bool CFG, int NB>
+template <bool A4, bool SYM, bool CFG, bool HS, int NB>
 hipError_t run(const GemmArgs& g, hipStream_t s) {
   const int rpt = CFG ? 64 : 128;
   const int T = (((CFG ? g.Mh : g.M) + rpt - 1) / rpt) * ((g.N + 16 * NB - 1) / (16 * NB));
@@ -664,27 +744,33 @@ hipError_t run(const GemmArgs& g, hipStream_t s) {
     g_cus = cus;
   }
   const int G = T < g_cus ? T : g_cus;
-  hipLaunchKernelGGL((k2_gemm<A4, SYM, CFG, NB>), dim3(G), dim3(kThreads), 0, s, g);
+  hipLaunchKernelGGL((k2_gemm<A4, SYM, CFG, HS, NB>), dim3(G), dim3(kThreads), 0, s, g);
   return hipGetLastError();
 }
 
 template <bool A4, bool SYM, bool CFG>
 hipError_t run_nb(const GemmArgs& g, hipStream_t s) {
   // 144-column tiles when they divide N, else 128.
-  if (g.N % 144 == 0) return run<A4, SYM, CFG, 9>(g, s);
-  return run<A4, SYM, CFG, 8>(g, s);
+  if (g.N % 144 == 0) return run<A4, SYM, CFG, false, 9>(g, s);
+  return run<A4, SYM, CFG, false, 8>(g, s);
 }
 
 template <bool A4>
-hipError_t run_mode(const GemmArgs& g, int sym, int cfg, hipStream_t s) {
+hipError_t run_mode(const GemmArgs& g, int sym, int cfg, int hs, hipStream_t s) {
+  // Single Hadamard: symmetric codes, 128 weight rows (64 channels) per tile
+  // so that every wave holds whole hi/lo pairs.
+  if (hs) {
+    if (!sym) return hipErrorInvalidValue;
+    return cfg ? run<A4, true, true, true, 8>(g, s) : run<A4, true, false, true, 8>(g, s);
+  }
   if (sym) return cfg ? run_nb<A4, true, true>(g, s) : run_nb<A4, true, false>(g, s);
   return cfg ? run_nb<A4, false, true>(g, s) : run_nb<A4, false, false>(g, s);
 }
 
 }  // namespace
 
-hipError_t launch_gemm(const GemmArgs& g, int a4, int sym, int cfg, hipStream_t s) {
-  return a4 ? run_mode<true>(g, sym, cfg, s) : run_mode<false>(g, sym, cfg, s);
+hipError_t launch_gemm(const GemmArgs& g, int a4, int sym, int cfg, int hs, hipStream_t s) {
+  return a4 ? run_mode<true>(g, sym, cfg, hs, s) : run_mode<false>(g, sym, cfg, hs, s);
 }
 
 }  // namespace ql

@@ -7,6 +7,8 @@
 // quantized on its own), round-half-even codes, and the weight-side LSB
 // truncation of TASQ (TASQ explainer, technical summary 2: a per-layer,
 // per-step operating precision over one stored set of codes).
+// For HQ-DM's single transform (activations only) the plan keeps H W_int^T
+// as two int8 planes (k0_fwht_split).
 // K3 is the guided prediction of the "Closing the Null Space" explainer,
 // problem statement.
 #include "ql_device.h"
@@ -121,6 +123,39 @@ __global__ __launch_bounds__(256) void k0_truncate_w(const uint4* in, int64_t n1
                       truncate4(v.w, keep));
 }
 
+// Single-Hadamard weights ([HQ-DM explainer 2.1: only the activations are
+// rotated]): V = H W_int^T row by row, exact (integers below 2^24 in fp32),
+// split into two int8 planes V = 128 * hi + lo with lo in [0, 127] and hi in
+// [-127, 127]. Output rows: for output channels 16g .. 16g+15, rows 32g ..
+// 32g+15 hold hi and rows 32g+16 .. 32g+31 hold lo, so a GEMM tile sees each
+// channel's two planes in adjacent 16-row fragments. Four codes per thread.
+template <int HB>
+__global__ __launch_bounds__(256) void k0_fwht_split(const uint32_t* codes, int K, int64_t nunits,
+                                                     uint8_t* out) {
+  const int lane = threadIdx.x & 63;
+  const int64_t idx = ((int64_t)blockIdx.x * 4 + (threadIdx.x >> 6)) * 64 + lane;
+  float e[4] = {0.f, 0.f, 0.f, 0.f};
+  if (idx < nunits) {
+    const uint32_t v = codes[idx];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) e[i] = (float)(int)(int8_t)((v >> (8 * i)) & 0xFFu);
+  }
+  fwht_block<HB>(e, lane);
+  if (idx >= nunits) return;
+  const int64_t n = (idx * 4) / K;
+  const int64_t k = idx * 4 - n * K;
+  uint32_t hi = 0, lo = 0;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int v = (int)e[i];
+    hi |= ((uint32_t)(v >> 7) & 0xFFu) << (8 * i);
+    lo |= ((uint32_t)(v & 127)) << (8 * i);
+  }
+  const int64_t row = 32 * (n >> 4) + (n & 15);
+  *reinterpret_cast<uint32_t*>(out + row * K + k) = hi;
+  *reinterpret_cast<uint32_t*>(out + (row + 16) * K + k) = lo;
+}
+
 // K3: out = yu + w * (yc - yu); yc = Y[e], yu = Y[e + half].
 __global__ __launch_bounds__(256) void k3_cfg(const float* Y, int64_t half, float w, float* out) {
   const int64_t stride = (int64_t)gridDim.x * 256;
@@ -187,6 +222,24 @@ hipError_t launch_truncate_weights(const uint8_t* in, int64_t nbytes, int k, uin
   hipLaunchKernelGGL(k0_truncate_w, dim3(blocks_for(threads, 256)), dim3(256), 0, s,
                      reinterpret_cast<const uint4*>(in), n16, keep, reinterpret_cast<uint4*>(out),
                      sw_in, sw_out, N);
+  return hipGetLastError();
+}
+
+hipError_t launch_fwht_split(const uint8_t* codes, int N, int K, int hb, uint8_t* out,
+                             hipStream_t s) {
+  if (K % 4 != 0 || K % hb != 0) return hipErrorInvalidValue;
+  const int64_t nunits = (int64_t)N * K / 4;
+  const dim3 grid(blocks_for(nunits, 256));
+  const uint32_t* in = reinterpret_cast<const uint32_t*>(codes);
+  switch (hb) {
+    case 4: hipLaunchKernelGGL((k0_fwht_split<4>), grid, dim3(256), 0, s, in, K, nunits, out); break;
+    case 8: hipLaunchKernelGGL((k0_fwht_split<8>), grid, dim3(256), 0, s, in, K, nunits, out); break;
+    case 16: hipLaunchKernelGGL((k0_fwht_split<16>), grid, dim3(256), 0, s, in, K, nunits, out); break;
+    case 32: hipLaunchKernelGGL((k0_fwht_split<32>), grid, dim3(256), 0, s, in, K, nunits, out); break;
+    case 64: hipLaunchKernelGGL((k0_fwht_split<64>), grid, dim3(256), 0, s, in, K, nunits, out); break;
+    case 128: hipLaunchKernelGGL((k0_fwht_split<128>), grid, dim3(256), 0, s, in, K, nunits, out); break;
+    default: return hipErrorInvalidValue;
+  }
   return hipGetLastError();
 }
 

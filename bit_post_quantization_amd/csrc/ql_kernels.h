@@ -34,7 +34,8 @@ struct GemmArgs {
   const float* w_scales;     // [N]
   float* Y;                  // [M,N] or [M/2,N]
   int32_t* dbg;              // [2,M,N] or nullptr
-  int M, N, K;
+  int M, N, K;               // N: weight rows (2 * roundup(Nout, 16) for single Hadamard)
+  int Nout;                  // output columns (N except for single Hadamard)
   int Mh;                    // M/2 with CFG pairing
   int64_t lda, ldw;          // bytes per row of A / W
   float guidance;
@@ -46,7 +47,8 @@ hipError_t launch_quantize(const QuantArgs& a, int x_bf16, int hadamard_block, i
                            hipStream_t s);
 
 // K2: GEMM + epilogue.
-hipError_t launch_gemm(const GemmArgs& g, int a4, int sym, int cfg, hipStream_t s);
+// hs: single-Hadamard weight planes (requires sym).
+hipError_t launch_gemm(const GemmArgs& g, int a4, int sym, int cfg, int hs, hipStream_t s);
 
 // K3: standalone CFG combine.
 hipError_t launch_cfg_combine(const float* Y, int64_t half_elems, float w, float* out,
@@ -59,6 +61,11 @@ hipError_t launch_weight_scales(const uint32_t* rowmax, int N, int mode, const i
                                 int nseg, float qw, float* sw, hipStream_t s);
 hipError_t launch_quantize_weights(const float* W, const float* sw, int N, int K, float qw,
                                    uint8_t* out, hipStream_t s);
+// Single-Hadamard weight planes: out has 2 * roundup(N, 16) rows of K bytes
+// (hi / lo interleaved per 16 channels; rows past N must be zeroed by the
+// caller). K % 4 == 0 and K % hadamard_block == 0.
+hipError_t launch_fwht_split(const uint8_t* codes, int N, int K, int hadamard_block, uint8_t* out,
+                             hipStream_t s);
 // Weight codes with the k low magnitude bits cleared (nbytes % 16 == 0,
 // 16-byte aligned), and a copy of the N weight scales.
 hipError_t launch_truncate_weights(const uint8_t* in, int64_t nbytes, int k, uint8_t* out,

@@ -16,7 +16,9 @@ struct qlinear_plan {
   ql_desc d;
   std::vector<int32_t> seg;  // host copy, n_segments + 1
   int device = -1;
-  uint8_t* wq = nullptr;     // weight codes, int8 [N,K]
+  uint8_t* wq = nullptr;     // GEMM weights: codes int8 [N,K], or the two planes of
+                             // H W_int^T, int8 [2 * roundup(N,16), K] (single Hadamard)
+  uint8_t* wint = nullptr;   // single Hadamard: the codes W_int, int8 [N,K]
   float* sw = nullptr;       // weight scales [N]
   ql::ReduceWs* ws = nullptr;
 };
@@ -75,6 +77,12 @@ ql_status check_desc(const ql_desc* d) {
     return fail(QL_ERR_ARG, "bad a_scale_mode %d", (int)d->a_scale_mode);
   if (d->x_dtype != QL_F32 && d->x_dtype != QL_BF16)
     return fail(QL_ERR_ARG, "bad x_dtype %d", (int)d->x_dtype);
+  if (d->single_hadamard != 0 && d->single_hadamard != 1)
+    return fail(QL_ERR_ARG, "single_hadamard = %d must be 0 or 1", d->single_hadamard);
+  if (d->single_hadamard && hb == 0)
+    return fail(QL_ERR_ARG, "single_hadamard needs hadamard_block > 0");
+  if (d->single_hadamard && d->a_scale_mode != QL_ASCALE_SYMMETRIC)
+    return fail(QL_ERR_UNSUPPORTED, "single_hadamard supports SYMMETRIC activation scales only");
   if (d->n_segments < 1) return fail(QL_ERR_ARG, "n_segments = %d must be >= 1", d->n_segments);
   if (d->n_segments > 1 && !d->seg_offsets)
     return fail(QL_ERR_ARG, "seg_offsets is NULL with n_segments = %d", d->n_segments);
@@ -86,6 +94,12 @@ ql_status check_desc(const ql_desc* d) {
       if (o[g + 1] <= o[g]) return fail(QL_ERR_ARG, "segment %d is empty or descending", g);
   }
   return QL_OK;
+}
+
+// Rows of the weight matrix the GEMM reads: N, or the hi/lo planes of every
+// 16 output channels for the single Hadamard.
+size_t gemm_weight_rows(const ql_desc& d) {
+  return d.single_hadamard ? (size_t)2 * (((size_t)d.N + 15) / 16 * 16) : (size_t)d.N;
 }
 
 ql_status check_plan(qlinear_plan_t p) {
@@ -101,6 +115,7 @@ void free_plan(struct qlinear_plan* p) {
   if (!p) return;
   if (p->wq) (void)hipFree(p->wq);
   if (p->sw) (void)hipFree(p->sw);
+  if (p->wint) (void)hipFree(p->wint);
   if (p->ws) (void)hipFree(p->ws);
   delete p;
 }
@@ -112,7 +127,8 @@ bool same_layer(const struct qlinear_plan* a, const struct qlinear_plan* b) {
   return x.N == y.N && x.K == y.K && x.w_bits == y.w_bits && x.a_bits == y.a_bits &&
          x.hadamard_block == y.hadamard_block && x.n_segments == y.n_segments &&
          x.w_scale_mode == y.w_scale_mode && x.a_scale_mode == y.a_scale_mode &&
-         x.x_dtype == y.x_dtype && a->seg == b->seg && a->device == b->device;
+         x.x_dtype == y.x_dtype && x.single_hadamard == y.single_hadamard && a->seg == b->seg &&
+         a->device == b->device;
 }
 
 // Enqueue view's weights = base's codes with k low magnitude bits cleared,
@@ -120,9 +136,16 @@ bool same_layer(const struct qlinear_plan* a, const struct qlinear_plan* b) {
 ql_status enqueue_lsb(struct qlinear_plan* view, const struct qlinear_plan* base, int k,
                       hipStream_t s) {
   const int64_t nbytes = (int64_t)base->d.N * base->d.K;
-  hipError_t e = ql::launch_truncate_weights(base->wq, nbytes, k, view->wq, base->sw, view->sw,
+  const bool single = base->d.single_hadamard != 0;
+  hipError_t e = ql::launch_truncate_weights(single ? base->wint : base->wq, nbytes, k,
+                                             single ? view->wint : view->wq, base->sw, view->sw,
                                              base->d.N, s);
   if (e != hipSuccess) return hip_fail(e, "truncating weight codes");
+  if (single) {  // rebuild the hi/lo planes from the truncated codes
+    e = ql::launch_fwht_split(view->wint, base->d.N, base->d.K, base->d.hadamard_block, view->wq,
+                              s);
+    if (e != hipSuccess) return hip_fail(e, "single-Hadamard weight planes");
+  }
   return QL_OK;
 }
 
@@ -164,7 +187,9 @@ ql_status qlinear_plan(const ql_desc* d, const float* W, void* stream, qlinear_p
   const int64_t N = d->N, K = d->K;
   // Weight codes are stored one per byte for both widths (4-bit codes lie
   // in [-7, 7]); the GEMM reads them without an unpack step.
+  const bool single = d->single_hadamard != 0;
   const size_t wbytes = (size_t)(N * K);
+  const size_t gbytes = single ? gemm_weight_rows(*d) * (size_t)K : wbytes;
   float* rot = nullptr;
   uint32_t* rowmax = nullptr;
   int32_t* segd = nullptr;
@@ -183,7 +208,8 @@ ql_status qlinear_plan(const ql_desc* d, const float* W, void* stream, qlinear_p
       return hip_fail(e, what);     \
     }                               \
   } while (0)
-  QL_TRY(hipMalloc(&p->wq, wbytes), "allocating weight codes");
+  QL_TRY(hipMalloc(&p->wq, gbytes), "allocating weight codes");
+  if (single) QL_TRY(hipMalloc(&p->wint, wbytes), "allocating unrotated weight codes");
   QL_TRY(hipMalloc(&p->sw, N * sizeof(float)), "allocating weight scales");
   QL_TRY(hipMalloc(&p->ws, sizeof(ql::ReduceWs)), "allocating reduction workspace");
   QL_TRY(hipMalloc(&rowmax, N * sizeof(uint32_t)), "allocating row maxima");
@@ -200,7 +226,7 @@ ql_status qlinear_plan(const ql_desc* d, const float* W, void* stream, qlinear_p
                         hipMemcpyHostToDevice, s),
          "copying segment offsets");
   const float* src = W;
-  if (d->hadamard_block) {
+  if (d->hadamard_block && !single) {
     QL_TRY(hipMalloc(&rot, N * K * sizeof(float)), "allocating rotation buffer");
     QL_TRY(hipMemcpyAsync(rot, W, N * K * sizeof(float), hipMemcpyDeviceToDevice, s),
            "copying W");
@@ -211,8 +237,13 @@ ql_status qlinear_plan(const ql_desc* d, const float* W, void* stream, qlinear_p
   QL_TRY(ql::launch_row_absmax(src, (int)N, (int)K, rowmax, s), "weight row maxima");
   QL_TRY(ql::launch_weight_scales(rowmax, (int)N, mode, segd, ngroups, qw, p->sw, s),
          "weight scales");
-  QL_TRY(ql::launch_quantize_weights(src, p->sw, (int)N, (int)K, qw, p->wq, s),
+  QL_TRY(ql::launch_quantize_weights(src, p->sw, (int)N, (int)K, qw, single ? p->wint : p->wq, s),
          "weight codes");
+  if (single) {
+    QL_TRY(hipMemsetAsync(p->wq, 0, gbytes, s), "clearing weight planes");
+    QL_TRY(ql::launch_fwht_split(p->wint, (int)N, (int)K, d->hadamard_block, p->wq, s),
+           "single-Hadamard weight planes");
+  }
   QL_TRY(hipStreamSynchronize(s), "synchronising plan stream");
 #undef QL_TRY
   cleanup();
@@ -238,9 +269,15 @@ ql_status qlinear_plan_lsb_view(qlinear_plan_t base, int32_t w_lsb_k, void* stre
   v->seg = base->seg;
   v->device = base->device;
   const size_t wbytes = (size_t)base->d.N * base->d.K;
-  hipError_t e = hipMalloc(&v->wq, wbytes);
+  const size_t gbytes = gemm_weight_rows(base->d) * (size_t)base->d.K;
+  hipError_t e = hipMalloc(&v->wq, gbytes);
   if (e == hipSuccess) e = hipMalloc(&v->sw, (size_t)base->d.N * sizeof(float));
   if (e == hipSuccess) e = hipMalloc(&v->ws, sizeof(ql::ReduceWs));
+  if (e == hipSuccess && base->d.single_hadamard) {
+    e = hipMalloc(&v->wint, wbytes);
+    // rows past N of the planes stay zero for the life of the view
+    if (e == hipSuccess) e = hipMemsetAsync(v->wq, 0, gbytes, s);
+  }
   if (e != hipSuccess) {
     free_plan(v);
     return hip_fail(e, "allocating view plan");
@@ -282,7 +319,8 @@ ql_status qlinear_plan_weights(qlinear_plan_t p, int8_t* w_codes, float* w_scale
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   hipError_t e;
   if (w_codes) {
-    e = hipMemcpyAsync(w_codes, p->wq, (size_t)p->d.N * p->d.K, hipMemcpyDeviceToDevice, s);
+    e = hipMemcpyAsync(w_codes, p->d.single_hadamard ? p->wint : p->wq, (size_t)p->d.N * p->d.K,
+                       hipMemcpyDeviceToDevice, s);
     if (e != hipSuccess) return hip_fail(e, "copying weight codes");
   }
   if (w_scales) {
@@ -345,7 +383,8 @@ ql_status qlinear_gemm(qlinear_plan_t p, const void* codes, const float* act_sca
   g.Y = Y;
   g.dbg = acc_dbg;
   g.M = M;
-  g.N = p->d.N;
+  g.N = (int)gemm_weight_rows(p->d);
+  g.Nout = p->d.N;
   g.K = p->d.K;
   g.Mh = cfg ? M / 2 : M;
   g.lda = p->d.a_bits == 4 ? p->d.K / 2 : p->d.K;
@@ -356,6 +395,7 @@ ql_status qlinear_gemm(qlinear_plan_t p, const void* codes, const float* act_sca
   g.inv_b = p->d.hadamard_block ? 1.0f / (float)p->d.hadamard_block : 1.0f;
   hipError_t e = ql::launch_gemm(g, p->d.a_bits == 4,
                                  p->d.a_scale_mode == QL_ASCALE_SYMMETRIC, cfg,
+                                 p->d.single_hadamard,
                                  reinterpret_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "launching gemm");
   return ok();

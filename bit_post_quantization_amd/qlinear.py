@@ -57,7 +57,8 @@ class Plan:
 
 def qlinear_plan(W, N: int, K: int, w_bits: int = 8, a_bits: int = 8, hadamard_block: int = 0,
                  seg_offsets: Optional[Sequence[int]] = None, w_scale: str = "channel",
-                 a_scale: str = "dual", x_dtype: str = "f32", stream=None) -> Plan:
+                 a_scale: str = "dual", x_dtype: str = "f32", stream=None,
+                 single_hadamard: bool = False) -> Plan:
     L = _lib.load()
     segs = None
     nseg = 1
@@ -68,12 +69,13 @@ def qlinear_plan(W, N: int, K: int, w_bits: int = 8, a_bits: int = 8, hadamard_b
                n_segments=nseg,
                seg_offsets=ctypes.cast(segs, ctypes.POINTER(ctypes.c_int32)) if segs else None,
                w_scale_mode=_WMODES[w_scale], a_scale_mode=_AMODES[a_scale],
-               x_dtype=_DTYPES[x_dtype])
+               x_dtype=_DTYPES[x_dtype], single_hadamard=int(bool(single_hadamard)))
     h = ctypes.c_void_p()
     check(L.qlinear_plan(ctypes.byref(d), _ptr(W), _stream(stream), ctypes.byref(h)))
     return Plan(h.value, dict(N=N, K=K, w_bits=w_bits, a_bits=a_bits,
                               hadamard_block=hadamard_block, seg_offsets=seg_offsets,
-                              w_scale=w_scale, a_scale=a_scale, x_dtype=x_dtype))
+                              w_scale=w_scale, a_scale=a_scale, x_dtype=x_dtype,
+                              single_hadamard=bool(single_hadamard)))
 
 
 def qlinear_plan_destroy(plan: Plan) -> None:
@@ -136,12 +138,13 @@ class QuantLinear:
     are allocated with torch on the current device (allocation only)."""
 
     def __init__(self, W, w_bits=8, a_bits=8, hadamard_block=0, seg_offsets=None,
-                 w_scale="channel", a_scale="dual", x_dtype="f32", stream=None):
+                 w_scale="channel", a_scale="dual", x_dtype="f32", stream=None,
+                 single_hadamard=False):
         N, K = W.shape
         self.N, self.K = int(N), int(K)
         self.a_bits, self.w_bits = a_bits, w_bits
         self.plan = qlinear_plan(W, self.N, self.K, w_bits, a_bits, hadamard_block, seg_offsets,
-                                 w_scale, a_scale, x_dtype, stream)
+                                 w_scale, a_scale, x_dtype, stream, single_hadamard)
         self.base = None
 
     def lsb_view(self, w_lsb_k: int, stream=None) -> "QuantLinear":

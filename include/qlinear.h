@@ -84,6 +84,11 @@ typedef struct {
   ql_wscale w_scale_mode;
   ql_ascale a_scale_mode;
   ql_dtype x_dtype;          /* dtype of X given to qlinear_quantize_act */
+  int32_t single_hadamard;   /* 0: rotate X and W (two-sided); 1: rotate X only
+                                (HQ-DM explainer 2.1, single transform): W is
+                                quantized unrotated and enters the product as
+                                H W_int^T. Needs hadamard_block > 0 and
+                                a_scale_mode SYMMETRIC (HQ-DM explainer 2.2). */
 } ql_desc;
 
 /* Shape rules checked by every call: K % 16 == 0 when both w_bits and
@@ -107,14 +112,20 @@ typedef struct {
  * descriptor or NULL pointer, QL_ERR_OOM, QL_ERR_HIP.
  */
 ql_status qlinear_plan(const ql_desc* d, const float* W, void* stream, qlinear_plan_t* out);
+/* With single_hadamard = 1 the plan quantizes W without rotation (scales and
+ * codes W_int as above) and keeps, besides W_int, the exact integer matrix
+ * V = H W_int^T (|V| <= B * qmax_w) as two int8 planes V = 128 hi + lo. The
+ * GEMM then computes acc = sum_k c[m,k] V[k,n] exactly and the epilogue
+ * y = ((float)acc * s) * s_w[n] * (1/B), (float) rounding the exact sum once:
+ * X W^T = (1/B) (X H)(H W^T) because H H = B I. */
 
 /* Free a plan's device memory. The caller ensures no enqueued work still
  * uses it (synchronise first). NULL is accepted. */
 ql_status qlinear_plan_destroy(qlinear_plan_t p);
 
 /* Copy a plan's weights out for inspection: w_codes DEVICE int8 [N,K]
- * (one code per byte), w_scales DEVICE fp32 [N]. Either may be NULL to skip
- * it. */
+ * (one code per byte; the unrotated W_int for single_hadamard), w_scales
+ * DEVICE fp32 [N]. Either may be NULL to skip it. */
 ql_status qlinear_plan_weights(qlinear_plan_t p, int8_t* w_codes, float* w_scales, void* stream);
 
 /*
@@ -193,7 +204,9 @@ ql_status qlinear_quantize_act(qlinear_plan_t p, const void* X, int32_t M, int32
  *   Y          : DEVICE fp32 out, [M,N] or [M/2,N].
  *   acc_dbg    : NULL, or DEVICE int32 [2,M,N] out: plane 0 = acc+, plane
  *                1 = acc- for every row (SYMMETRIC: plane 0 = acc+ + acc-,
- *                plane 1 = 0). For parity checks; costs extra stores.
+ *                plane 1 = 0; single_hadamard: the exact sum is 128 * plane 0
+ *                + plane 1, the products with the hi and lo planes). For
+ *                parity checks; costs extra stores.
  */
 ql_status qlinear_gemm(qlinear_plan_t p, const void* codes, const float* act_scales, int32_t M,
                        int32_t cfg, float w, float* Y, int32_t* acc_dbg, void* stream);

@@ -115,6 +115,63 @@ def check_layer(torch, X, W, *, M, K, N, w_bits=8, a_bits=8, B=0, seg=None, w_sc
     return dict(codes=st, y_rel=e, y_exact=exact)
 
 
+def check_single(torch, X, W, *, M, K, N, B, w_bits=8, a_bits=8, cfg=0, guidance=4.0,
+                 w_scale="channel", seg=None, x_dtype="f32", rows=None, w_lsb_k=0, tag=""):
+    """HQ-DM single Hadamard (X rotated, W not) on the GPU against the oracle:
+    unrotated weight codes and scales, activation codes, the exact int64
+    contraction with H W_int^T (from the GPU's hi/lo plane sums) and Y."""
+    from bit_post_quantization_amd import QuantLinear
+    say(f"[single] {tag} M={M} K={K} N={N} B={B} w{w_bits}a{a_bits} cfg={cfg} wk={w_lsb_k}")
+    ql = QuantLinear(_dev(torch, W), w_bits=w_bits, a_bits=a_bits, hadamard_block=B,
+                     seg_offsets=seg, w_scale=w_scale, a_scale="symmetric", x_dtype=x_dtype,
+                     single_hadamard=True)
+    wp = oracle.SingleHadamardPlan(W, w_bits, B, mode=w_scale, seg_offsets=seg)
+    check_weights(torch, ql, wp)
+    if w_lsb_k:
+        view = ql.lsb_view(w_lsb_k)
+        ql.plan.destroy()
+        ql, wp = view, wp.truncated(w_lsb_k)
+        check_weights(torch, ql, wp)
+    Xd = _dev(torch, X) if x_dtype == "f32" else _dev(torch, X.view(np.int16))
+    codes_d, s_d = ql.quantize(Xd)
+    torch.cuda.synchronize()
+    codes_g = unpack_codes(codes_d.cpu().numpy(), K, a_bits)
+    s_g = s_d.cpu().numpy()
+    x32 = oracle.bf16_to_f32(X) if x_dtype == "bf16" else X
+    x_rot = oracle.rotate(x32, B)
+    s_o = oracle.act_scales(x_rot, a_bits, "symmetric")
+    assert np.array_equal(s_g.view(np.uint32), s_o.view(np.uint32)), "act scales"
+    st = compare_codes(codes_g, oracle.quantize_act(x_rot, s_o, a_bits), x_rot, s_o)
+    assert_codes(st)
+    Mo = M // 2 if cfg else M
+    Yd = torch.empty((Mo, N), dtype=torch.float32, device="cuda")
+    dbg = torch.empty((2, M, N), dtype=torch.int32, device="cuda")
+    ql.gemm(codes_d, s_d, cfg=cfg, w=guidance, Y=Yd, acc_dbg=dbg)
+    Yd2 = torch.empty_like(Yd)
+    ql.gemm(codes_d, s_d, cfg=cfg, w=guidance, Y=Yd2)
+    torch.cuda.synchronize()
+    assert torch.equal(Yd.view(torch.int32), Yd2.view(torch.int32)), "Y differs without acc dump"
+    out_rows = np.arange(Mo) if rows is None else np.asarray(rows)
+    acc_rows = np.concatenate([out_rows, out_rows + M // 2]) if cfg else out_rows
+    idx = torch.from_numpy(acc_rows).cuda()
+    hi = dbg[0].index_select(0, idx).cpu().numpy().astype(np.int64)
+    lo = dbg[1].index_select(0, idx).cpu().numpy().astype(np.int64)
+    acc_o = oracle.gemm_int64(codes_g, wp.v, acc_rows)
+    assert np.array_equal(128 * hi + lo, acc_o), "exact accumulators"
+    y_o = oracle.epilogue_single(acc_o, s_g[0], wp.scales, B)
+    if cfg:
+        h = out_rows.size
+        ref = oracle.cfg_combine(y_o[:h], y_o[h:], guidance)
+    else:
+        ref = y_o
+    Y_g = Yd.index_select(0, torch.from_numpy(out_rows).cuda()).cpu().numpy()
+    e = assert_close(Y_g, ref, "Y")
+    exact = np.array_equal(Y_g.view(np.uint32), ref.view(np.uint32))
+    say(f"  codes {st}; acc exact; Y max rel err {e:.3g}; bit-exact={exact}; "
+        f"max |acc| {np.abs(acc_o).max()}")
+    return dict(y_exact=exact, acc_max=int(np.abs(acc_o).max()))
+
+
 # ---------------------------------------------------------------- small ----
 
 def test_config1_full(torch):
@@ -173,6 +230,51 @@ def test_weight_lsb_view(torch, w_bits, a_bits, wk, B, a_scale, seg):
     check_layer(torch, X, W, M=M, K=K, N=N, w_bits=w_bits, a_bits=a_bits, B=B, a_scale=a_scale,
                 seg=seg, w_scale="segment" if seg else "channel", cfg=1, w_lsb_k=wk,
                 tag=f"wlsb{wk}")
+
+
+@pytest.mark.parametrize("M,K,N,B,w_bits,a_bits,cfg", [
+    (130, 512, 96, 128, 8, 8, 1), (200, 256, 100, 16, 8, 8, 0), (64, 1024, 33, 128, 4, 4, 1),
+    (97, 128, 80, 4, 8, 4, 0), (2, 64, 1, 32, 4, 8, 1)])
+def test_single_hadamard(torch, M, K, N, B, w_bits, a_bits, cfg):
+    X = synth.gelu_with_outliers(23, f"single/{M}{K}{N}{B}", M, K)
+    W = synth.weight_normal(23, f"single/W{M}{K}{N}{B}", N, K)
+    check_single(torch, X, W, M=M, K=K, N=N, B=B, w_bits=w_bits, a_bits=a_bits, cfg=cfg,
+                 tag="single")
+
+
+def test_single_hadamard_extremes(torch):
+    # A bent sign pattern b of 64 entries (the inner product of the two 3-bit
+    # halves of the index) has a flat transform: |H b| = 8 everywhere. Rows
+    # built from +-b per block give activation and weight codes of +-127 and
+    # |H W_int^T| = 1016 throughout, so at the largest K the exact sums reach
+    # 127 * 1016 * 65536 > 2^31: only the hi/lo split keeps them exact.
+    M, K, N, B = 8, 65536, 16, 64
+    i = np.arange(B)
+    b = np.where(np.array([bin((j & 7) & (j >> 3)).count("1") & 1 for j in i]) == 1, -1.0, 1.0)
+    rng = np.random.default_rng(24)
+    sx = np.where(rng.random((M, K // B)) < 0.5, -1.0, 1.0)
+    sw = np.where(rng.random((N, K // B)) < 0.5, -1.0, 1.0)
+    sx[0] = sw[0]  # row 0 against channel 0: every block adds +127 * 1016 * 64
+    X = (np.repeat(sx, B, axis=1) * np.tile(b, K // B)).astype(np.float32)
+    W = (np.repeat(sw, B, axis=1) * np.tile(b, K // B) * 0.01).astype(np.float32)
+    r = check_single(torch, X, W, M=M, K=K, N=N, B=B, tag="extremes")
+    assert r["acc_max"] == 127 * 1016 * K > 2 ** 31
+
+
+def test_single_hadamard_weight_view(torch):
+    M, K, N, B = 96, 1152, 144, 128
+    X = synth.silu_normal(25, "single/view/X", M, K)
+    W = synth.weight_normal(25, "single/view/W", N, K)
+    check_single(torch, X, W, M=M, K=K, N=N, B=B, cfg=1, w_lsb_k=3, tag="view")
+
+
+def test_single_hadamard_rejects_dual_scales(torch):
+    from bit_post_quantization_amd import QLError, QuantLinear
+    W = _dev(torch, synth.weight_normal(26, "single/rej", 32, 128))
+    with pytest.raises(QLError):
+        QuantLinear(W, hadamard_block=128, a_scale="dual", single_hadamard=True)
+    with pytest.raises(QLError):
+        QuantLinear(W, hadamard_block=0, a_scale="symmetric", single_hadamard=True)
 
 
 def test_weight_lsb_update(torch):
