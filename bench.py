@@ -37,7 +37,7 @@ def parse():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=50)
     p.add_argument("--warmup", type=int, default=10)
-    p.add_argument("--workload", default="mlp", help="mlp (default) | block | c3 | c4 | c4g | c5 | c6")
+    p.add_argument("--workload", default="mlp", help="mlp (default) | block | c3 | c3s | c4 | c4g | c5 | c6")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=12.0,
                    help="approximate CPU time budget of the oracle baseline")
@@ -58,6 +58,8 @@ def layers_for(name):
     if name in ("c3", "c4"):
         wl = configs.WORKLOADS[name]
         return wl, list(wl.layers)
+    if name == "c3s":
+        return configs.WORKLOADS["c3"], list(configs.c3_single())
     if name == "c4g":
         # The MM-DiT stack with activation bits from the greedy allocation
         # (library host code) instead of the seeded mask.
@@ -82,14 +84,18 @@ class Layer:
         seg = L.seg_offsets()
         self.ql = QuantLinear(Wd, w_bits=L.w_bits, a_bits=L.a_bits, hadamard_block=L.hadamard_block,
                               seg_offsets=None if seg is None else seg.tolist(),
-                              w_scale=L.w_scale, a_scale=L.a_scale, x_dtype=L.x_dtype)
+                              w_scale=L.w_scale, a_scale=L.a_scale, x_dtype=L.x_dtype,
+                              single_hadamard=L.single_hadamard)
         del Wd
         self.codes = self.ql.alloc_codes(self.M)
         self.scales = torch.empty(2, dtype=torch.float32, device="cuda")
         rows = self.M // 2 if L.cfg else self.M
         self.Y = torch.empty((rows, L.N), dtype=torch.float32, device="cuda")
         # algorithmic work
-        self.mfma_ops = (2 if L.a_scale == "dual" else 1) * 2.0 * self.M * L.N * L.K
+        # MFMA work executed: two products per output with DualScale (both
+        # polarity planes) or with the single Hadamard (hi and lo planes).
+        planes = 2 if (L.a_scale == "dual" or L.single_hadamard) else 1
+        self.mfma_ops = planes * 2.0 * self.M * L.N * L.K
         self.eff_ops = 2.0 * self.M * L.N * L.K
         xbytes = 2 if L.x_dtype == "bf16" else 4
         self.quant_bytes = self.M * L.K * (xbytes + L.a_bits / 8.0)
@@ -496,6 +502,8 @@ def main():
             "workload": {"mlp": "DiT-XL/2 MLP fc1 1152->4608 + fc2 4608->1152",
                          "block": "DiT-XL/2 block QKV+proj+fc1+fc2",
                          "c3": "DiT-XL/2 block W4A4 + Hadamard-128",
+                         "c3s": "DiT-XL/2 block W4A4, single Hadamard-128 on X only "
+                                "(W as H W_int^T), symmetric activations",
                          "c4": "MM-DiT SegLinear layers W4 A4/A8",
                          "c4g": "MM-DiT SegLinear layers W4, A4/A8 by the greedy allocation"
                          }[args.workload],

@@ -481,6 +481,19 @@ def test_config3_dit_w4a4_hadamard(torch, li):
     _run_workload_layer(torch, "c3", li)
 
 
+@pytest.mark.timeout(600)
+@pytest.mark.parametrize("li", range(4))
+def test_config3_single_hadamard(torch, li):
+    wl = configs.WORKLOADS["c3"]
+    L = configs.c3_single()[li]
+    X = configs.make_x(wl, L)
+    W = configs.make_w(wl, L)
+    rows = sample_rows(wl.M, True, 48, seed=200 + li)
+    check_single(torch, X, W, M=wl.M, K=L.K, N=L.N, B=L.hadamard_block, w_bits=L.w_bits,
+                 a_bits=L.a_bits, cfg=int(L.cfg), guidance=L.guidance, rows=rows,
+                 tag=f"c3s/{L.name}")
+
+
 @pytest.mark.timeout(900)
 @pytest.mark.parametrize("li", range(4))
 def test_config4_mmdit_segments(torch, li):

@@ -35,6 +35,7 @@ class Layer:
     x_kind: str = "silu"              # "silu" | "gelu_outliers" | "bf16_normal"
     cfg: bool = False
     guidance: float = 4.0
+    single_hadamard: bool = False     # rotate X only (W enters as H W_int^T)
 
     def seg_offsets(self) -> Optional[np.ndarray]:
         if self.n_segments <= 1:
@@ -79,6 +80,14 @@ def _c3() -> Workload:
         M=4096,
         layers=tuple(Layer(n, k, nn, w_bits=4, a_bits=4, hadamard_block=128,
                            x_kind="gelu_outliers", cfg=True) for n, k, nn in DIT_SHAPES))
+
+
+def c3_single() -> Tuple[Layer, ...]:
+    """The c3 stack with HQ-DM's single transform: X rotated, W quantized
+    unrotated, symmetric activation scales (same inputs as c3)."""
+    import dataclasses
+    return tuple(dataclasses.replace(L, a_scale="symmetric", single_hadamard=True)
+                 for L in WORKLOADS["c3"].layers)
 
 
 def c4_a8_mask(seed: int = SEED) -> np.ndarray:
