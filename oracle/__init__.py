@@ -315,6 +315,63 @@ class WeightPlan:
         return v
 
 
+class InputSegmentedPlan:
+    """[SQ] 2.A, input segmentation: the input is a concatenation of branches
+    along K, X = [X_0 | X_1 | ...] at k_offsets, and each branch is quantized
+    apart: its weight columns W[:, o_j:o_j+1] get their own scales (per
+    channel, output segment or tensor) and, in quantize_activations_segmented,
+    its activations their own DualScale pair."""
+
+    def __init__(self, W: np.ndarray, w_bits: int, k_offsets: Sequence[int], B: int = 0,
+                 mode: str = "channel", seg_offsets: Optional[Sequence[int]] = None):
+        self.w_bits, self.B = w_bits, B
+        self.k_offsets = [int(v) for v in k_offsets]
+        W = np.ascontiguousarray(W, dtype=np.float32)
+        self.parts = [WeightPlan(W[:, a:b], w_bits, B=B, mode=mode, seg_offsets=seg_offsets)
+                      for a, b in zip(self.k_offsets[:-1], self.k_offsets[1:])]
+        self.codes = np.concatenate([p.codes for p in self.parts], axis=1)
+        self.scales = np.stack([p.scales for p in self.parts])  # [S, N]
+
+    def truncated(self, k: int) -> "InputSegmentedPlan":
+        v = InputSegmentedPlan.__new__(InputSegmentedPlan)
+        v.w_bits, v.B, v.k_offsets = self.w_bits, self.B, self.k_offsets
+        v.parts = [p.truncated(k) for p in self.parts]
+        v.codes = np.concatenate([p.codes for p in v.parts], axis=1)
+        v.scales = self.scales
+        return v
+
+
+def quantize_activations_segmented(X: np.ndarray, a_bits: int, k_offsets: Sequence[int],
+                                   B: int = 0, mode: str = "dual", lsb_k: int = 0,
+                                   static_scales: Optional[np.ndarray] = None,
+                                   bf16: bool = False):
+    """Every branch quantized on its own. Returns (codes int8 [M,K], scales [S,2])."""
+    codes, scales = [], []
+    for j, (a, b) in enumerate(zip(k_offsets[:-1], k_offsets[1:])):
+        st = None if static_scales is None else np.asarray(static_scales, np.float32)[j]
+        c, sc = quantize_activations(X[:, a:b], a_bits, B=B, mode=mode, lsb_k=lsb_k,
+                                     static_scales=st, bf16=bf16)
+        codes.append(c)
+        scales.append(sc)
+    return np.concatenate(codes, axis=1), np.stack(scales)
+
+
+def linear_segmented_rows(codes: np.ndarray, s: np.ndarray, wp: InputSegmentedPlan,
+                          rows: Sequence[int], mode: str = "dual"):
+    """y [len(rows), N] = sum over branches, in branch order, of each branch's
+    epilogue (fp32 adds), then the rotation's 1/B; plus the per-branch
+    accumulators [(acc+, acc-), ...]."""
+    y, accs = None, []
+    for j, (a, b) in enumerate(zip(wp.k_offsets[:-1], wp.k_offsets[1:])):
+        accp, accn = gemm_dual(codes[:, a:b], wp.parts[j].codes, rows)
+        accs.append((accp, accn))
+        yj = epilogue(accp, accn, s[j], wp.scales[j], 0, mode)
+        y = yj if y is None else (y + yj).astype(np.float32)
+    if wp.B:
+        y = (y * np.float32(1.0 / wp.B)).astype(np.float32)
+    return y, accs
+
+
 def quantize_activations(X: np.ndarray, a_bits: int, B: int = 0, mode: str = "dual",
                          lsb_k: int = 0, static_scales: Optional[np.ndarray] = None,
                          bf16: bool = False):

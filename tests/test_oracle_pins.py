@@ -605,3 +605,53 @@ def test_single_hadamard_exact_on_grid(orc):
     ref = (exact.astype(np.float64) * (s * sw / B)).astype(np.float32)
     assert np.array_equal(y, ref)
     assert np.allclose(y, X.astype(np.float64) @ W.astype(np.float64).T, rtol=0, atol=1e-6)
+
+
+# --------------------------------------------- SegLinear input segments -----
+
+def test_input_segments_one_branch_is_unsegmented(orc):
+    X = synth.gelu_with_outliers(31, "kseg/one/X", 40, 256)
+    W = synth.weight_normal(31, "kseg/one/W", 24, 256)
+    for B, mode in [(0, "dual"), (128, "dual"), (16, "symmetric")]:
+        wp = orc.WeightPlan(W, 8, B=B)
+        sp = orc.InputSegmentedPlan(W, 8, [0, 256], B=B)
+        assert np.array_equal(sp.codes, wp.codes) and np.array_equal(sp.scales[0], wp.scales)
+        c1, s1 = orc.quantize_activations(X, 8, B=B, mode=mode)
+        c2, s2 = orc.quantize_activations_segmented(X, 8, [0, 256], B=B, mode=mode)
+        assert np.array_equal(c1, c2) and np.array_equal(s1, s2[0])
+        rows = np.arange(40)
+        y1, _, _ = orc.linear_rows(c1, s1, wp, rows, mode)
+        y2, _ = orc.linear_segmented_rows(c2, s2, sp, rows, mode)
+        assert np.array_equal(y1.view(np.uint32), y2.view(np.uint32))
+
+
+def test_input_segments_exact_on_grid(orc):
+    # Two branches on their own quantization grids (power-of-two scales that
+    # differ by 2^8 between the branches, max codes reached in each): the
+    # segmented layer returns X W^T rounded once, from the integers alone.
+    # One shared scale pair would round the small branch's values to zero.
+    rng = np.random.default_rng(32)
+    M, N, offs = 12, 20, [0, 128, 384]
+    s_b = [2.0 ** -3, 2.0 ** -11]
+    w_b = [2.0 ** -7, 2.0 ** -5]
+    C = rng.integers(-127, 128, (M, 384))
+    C[0, 0] = C[0, 128] = 127
+    C[1, 1] = C[1, 129] = -127
+    Wi = rng.integers(-127, 128, (N, 384))
+    Wi[:, 0] = Wi[:, 128] = 127
+    X = np.concatenate([C[:, :128] * s_b[0], C[:, 128:] * s_b[1]], axis=1).astype(np.float32)
+    W = np.concatenate([Wi[:, :128] * w_b[0], Wi[:, 128:] * w_b[1]], axis=1).astype(np.float32)
+    wp = orc.InputSegmentedPlan(W, 8, offs)
+    codes, s = orc.quantize_activations_segmented(X, 8, offs)
+    assert np.array_equal(codes, C) and np.array_equal(wp.codes, Wi)
+    assert s.tolist() == [[s_b[0], s_b[0]], [s_b[1], s_b[1]]]
+    y, accs = orc.linear_segmented_rows(codes, s, wp, np.arange(M))
+    exact = (C[:, :128] @ Wi[:, :128].T) * (s_b[0] * w_b[0]) + \
+            (C[:, 128:] @ Wi[:, 128:].T) * (s_b[1] * w_b[1])
+    assert np.array_equal(y, exact.astype(np.float32))
+    ap, an = accs[1]
+    cp = np.maximum(C[:, 128:], 0)
+    assert np.array_equal(ap, cp @ Wi[:, 128:].T) and np.array_equal(an, (C[:, 128:] - cp) @ Wi[:, 128:].T)
+    # a single scale pair over the concatenation loses the second branch
+    c1, s1 = orc.quantize_activations(X, 8)
+    assert np.count_nonzero(c1[:, 128:]) == 0
