@@ -33,6 +33,7 @@ class QlDesc(ctypes.Structure):
         ("seg_offsets", ctypes.POINTER(ctypes.c_int32)),
         ("w_scale_mode", ctypes.c_int), ("a_scale_mode", ctypes.c_int),
         ("x_dtype", ctypes.c_int), ("single_hadamard", ctypes.c_int32),
+        ("n_k_segments", ctypes.c_int32), ("k_seg_offsets", ctypes.POINTER(ctypes.c_int32)),
     ]
 
 

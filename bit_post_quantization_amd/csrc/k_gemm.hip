@@ -57,7 +57,7 @@ typedef __attribute__((address_space(3))) void lds_void;
 template <int V>
 using IC = std::integral_constant<int, V>;
 
-constexpr int kThreads = 512;
+constexpr int kThreads = kGemmThreads;
 constexpr int BK = 128;                 // K elements per ring stage
 constexpr int kStages = 4;              // ring depth (= unroll of the step loop)
 constexpr unsigned kOOB = 0x80000000u;  // offset beyond every buffer: loads return 0
@@ -186,16 +186,19 @@ __device__ __forceinline__ v4i mfma(v4i a, v4i b, v4i c) {
 
 // y from the two accumulators in the documented order, no contraction.
 template <bool SYM>
-__device__ __forceinline__ float epi(int accp, int accn, float sp, float sn, float sw, float inv_b) {
-  float y;
+__device__ __forceinline__ float epi_part(int accp, int accn, float sp, float sn, float sw) {
   if constexpr (SYM) {
-    y = __fmul_rn(__fmul_rn((float)accp, sp), sw);
+    return __fmul_rn(__fmul_rn((float)accp, sp), sw);
   } else {
     const float tp = __fmul_rn((float)accp, sp);
     const float tn = __fmul_rn((float)accn, sn);
-    y = __fmul_rn(__fadd_rn(tp, tn), sw);
+    return __fmul_rn(__fadd_rn(tp, tn), sw);
   }
-  return __fmul_rn(y, inv_b);
+}
+
+template <bool SYM>
+__device__ __forceinline__ float epi(int accp, int accn, float sp, float sn, float sw, float inv_b) {
+  return __fmul_rn(epi_part<SYM>(accp, accn, sp, sn, sw), inv_b);
 }
 
 // Tiles of workgroup b. When grid and tile counts divide by 8, each XCD
@@ -302,7 +305,7 @@ __device__ __forceinline__ void schedule_step() {
 // pair w + 8, so a step's body has no branches and every step issues the
 // same number of loads: the compiler can then prove from the explicit
 // waits below that each LDS read finds its data landed.
-template <bool A4, bool SYM, bool CFG, bool HS, int NB, int CG, bool TW>
+template <bool A4, bool SYM, bool CFG, bool HS, bool KS, int NB, int CG, bool TW>
 __device__ __forceinline__ void gemm_wave(const GemmArgs& g, int wave, int lane, uint8_t* st0,
                                           uint8_t* st1, uint8_t* st2, uint8_t* st3) {
   using Lay = Layout<A4, NB>;
@@ -483,10 +486,29 @@ __device__ __forceinline__ void gemm_wave(const GemmArgs& g, int wave, int lane,
     schedule_step<NBW, kReads, kValu, !SYM>();
   };
 
-  const float sp = g.act_scales[0];
-  const float sn = g.act_scales[1];
+  // Scales of the last input branch (the only one without input branches).
+  const int jl = KS ? g.nks - 1 : 0;
+  const float sp = g.act_scales[2 * jl];
+  const float sn = g.act_scales[2 * jl + 1];
+  const float* const w_scales_last = g.w_scales + (int64_t)jl * g.Nout;
   const int i16 = lane & 15;
   const int rsub = (lane >> 4) * 4;
+  // Input branches: the fp32 sum of the finished branches' epilogue parts
+  // per output lives in this thread's slice of the plan's workspace (slot s
+  // of the thread at [block][s][thread]), written at each branch end and read
+  // back (from L2) by the next branch end or by the tile epilogue. Also the
+  // current branch and the K-step at which it ends.
+  static_assert(!KS || 2 * NBW * 4 <= kYSlots, "partial-sum slots");
+  float* const yws = KS ? g.ypart_ws + (int64_t)blockIdx.x * kYSlots * kThreads + threadIdx.x
+                        : nullptr;
+  auto yslot = [&](int fi, int jj, int r) __attribute__((always_inline)) {
+    return yws + ((fi * NBW + jj) * 4 + r) * kThreads;
+  };
+  auto yload = [&](int fi, int jj, int r) __attribute__((always_inline)) {
+    return __hip_atomic_load(yslot(fi, jj, r), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  };
+  int cur_seg = 0;
+  int seg_end = KS ? g.ks_end[0] : 0;
 
   // (acc+, acc-) of accumulator slot (fi, jj, r), shifted back to code units.
   auto accs = [&](int fi, int jj, int r, int& ap, int& an) __attribute__((always_inline)) {
@@ -502,6 +524,73 @@ __device__ __forceinline__ void gemm_wave(const GemmArgs& g, int wave, int lane,
   // stores (rows past the end and columns past N are dropped by the range
   // check), so no store waits on another and there are no per-element
   // branches.
+  // Accumulator dump (testing aid): planes 2j and 2j + 1 of [2 * nks, M, N]
+  // hold (acc+, acc-) of input branch j.
+  auto dump_acc = [&](int m0, const unsigned (&coff)[NBW], int j) __attribute__((always_inline)) {
+    const int64_t plane = (int64_t)g.M * g.N;
+#pragma unroll
+    for (int fi = 0; fi < 2; ++fi)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        bool ok;
+        const int grow = a_row(m0, 2 * band + fi, rsub + r, ok);
+        if (!ok) continue;
+#pragma unroll
+        for (int jj = 0; jj < NBW; ++jj) {
+          if (coff[jj] == kOOB) continue;
+          const int64_t e = (int64_t)grow * g.N + (coff[jj] >> 2);
+          int ap, an;
+          accs(fi, jj, r, ap, an);
+          g.dbg[2 * j * plane + e] = ap;
+          g.dbg[(2 * j + 1) * plane + e] = an;
+        }
+      }
+  };
+
+  // End of input branch cur_seg inside a tile: add its epilogue part to
+  // ypart (fp32, branch order) and let the accumulators restart. The scale
+  // loads and any dump stores drain before the K loop goes on.
+  auto fold = [&](int ti) __attribute__((always_inline)) {
+    int m0, n0;
+    coords(ti, m0, n0);
+    const int j = cur_seg;
+    const float spj = g.act_scales[2 * j];
+    const float snj = g.act_scales[2 * j + 1];
+    float swj[NBW];
+    unsigned coff[NBW];
+#pragma unroll
+    for (int jj = 0; jj < NBW; ++jj) {
+      const int col = n0 + 16 * (J0 + jj) + i16;
+      swj[jj] = g.w_scales[(int64_t)j * g.Nout + min(col, g.N - 1)];
+      coff[jj] = col < g.N ? 4u * (unsigned)col : kOOB;
+    }
+#pragma unroll
+    for (int jj = 0; jj < NBW; ++jj) asm volatile("" ::"v"(swj[jj]));
+    // One accumulator row r at a time (8 partial sums in flight), so the
+    // reloads do not all occupy registers at once.
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      float old[2][NBW];
+#pragma unroll
+      for (int fi = 0; fi < 2; ++fi)
+#pragma unroll
+        for (int jj = 0; jj < NBW; ++jj) old[fi][jj] = j > 0 ? yload(fi, jj, r) : 0.0f;
+#pragma unroll
+      for (int fi = 0; fi < 2; ++fi)
+#pragma unroll
+        for (int jj = 0; jj < NBW; ++jj) {
+          int ap, an;
+          accs(fi, jj, r, ap, an);
+          float y = epi_part<SYM>(ap, an, spj, snj, swj[jj]);
+          if (j > 0) y = __fadd_rn(old[fi][jj], y);
+          if constexpr (KS) *yslot(fi, jj, r) = y;
+        }
+      asm volatile("" ::: "memory");
+    }
+    if (g.dbg) dump_acc(m0, coff, j);
+    wait_vmcnt<0>();
+  };
+
   // Single Hadamard: fragments (J0 + 2p, J0 + 2p + 1) hold the hi and lo
   // planes of the same 16 output channels; the exact sum 128 * hi + lo is
   // formed in fp64 (|sum| < 2^53) and rounded once to fp32.
@@ -587,26 +676,48 @@ __device__ __forceinline__ void gemm_wave(const GemmArgs& g, int wave, int lane,
 #pragma unroll
     for (int jj = 0; jj < NBW; ++jj) {
       const int col = n0 + 16 * (J0 + jj) + i16;
-      sw[jj] = g.w_scales[min(col, g.N - 1)];
+      sw[jj] = w_scales_last[min(col, g.N - 1)];
       coff[jj] = col < g.N ? 4u * (unsigned)col : kOOB;
     }
 #pragma unroll
     for (int jj = 0; jj < NBW; ++jj) asm volatile("" ::"v"(sw[jj]));
+    // With input branches, the finished branches' sums of accumulator row r
+    // (reloaded one row at a time).
+    float yp[KS ? 2 : 1][KS ? NBW : 1];
+    auto load_yp = [&](int r) __attribute__((always_inline)) {
+      if constexpr (KS) {
+        asm volatile("" ::: "memory");
+#pragma unroll
+        for (int fi = 0; fi < 2; ++fi)
+#pragma unroll
+          for (int jj = 0; jj < NBW; ++jj) yp[fi][jj] = yload(fi, jj, r);
+      }
+    };
+    // Output of slot (fi, jj, r): with input branches, the finished
+    // branches' sum plus this branch's part, then the rotation's 1/B.
+    auto yout = [&](int fi, int jj, int r) __attribute__((always_inline)) {
+      int ap, an;
+      accs(fi, jj, r, ap, an);
+      if constexpr (KS) {
+        const float y = __fadd_rn(yp[fi][jj], epi_part<SYM>(ap, an, sp, sn, sw[jj]));
+        return __fmul_rn(y, g.inv_b);
+      } else {
+        return epi<SYM>(ap, an, sp, sn, sw[jj], g.inv_b);
+      }
+    };
     const int rows_here = min(RPT, (CFG ? g.Mh : g.M) - m0);
     const __amdgpu_buffer_rsrc_t ry =
         make_rsrc(g.Y + (int64_t)m0 * g.N, (uint32_t)rows_here * (uint32_t)g.N * 4u);
     const unsigned rowb = (unsigned)g.N * 4u;
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
+      load_yp(r);
       if constexpr (CFG) {
         const unsigned ro = (unsigned)(16 * band + rsub + r) * rowb;
 #pragma unroll
         for (int jj = 0; jj < NBW; ++jj) {
-          int cp, cn, up, un;
-          accs(0, jj, r, cp, cn);
-          accs(1, jj, r, up, un);
-          const float yc = epi<SYM>(cp, cn, sp, sn, sw[jj], g.inv_b);
-          const float yu = epi<SYM>(up, un, sp, sn, sw[jj], g.inv_b);
+          const float yc = yout(0, jj, r);
+          const float yu = yout(1, jj, r);
           const float d = __fsub_rn(yc, yu);
           const float t = __fmul_rn(g.guidance, d);
           __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(__fadd_rn(yu, t)), ry,
@@ -617,36 +728,13 @@ __device__ __forceinline__ void gemm_wave(const GemmArgs& g, int wave, int lane,
         for (int fi = 0; fi < 2; ++fi) {
           const unsigned ro = (unsigned)(16 * (2 * band + fi) + rsub + r) * rowb;
 #pragma unroll
-          for (int jj = 0; jj < NBW; ++jj) {
-            int ap, an;
-            accs(fi, jj, r, ap, an);
-            __builtin_amdgcn_raw_buffer_store_b32(
-                __float_as_uint(epi<SYM>(ap, an, sp, sn, sw[jj], g.inv_b)), ry, ro + coff[jj],
-                0, 0);
-          }
+          for (int jj = 0; jj < NBW; ++jj)
+            __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(yout(fi, jj, r)), ry,
+                                                  ro + coff[jj], 0, 0);
         }
       }
     }
-    if (g.dbg) {  // accumulator dump (testing aid)
-      const int64_t plane = (int64_t)g.M * g.N;
-#pragma unroll
-      for (int fi = 0; fi < 2; ++fi)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          bool ok;
-          const int grow = a_row(m0, 2 * band + fi, rsub + r, ok);
-          if (!ok) continue;
-#pragma unroll
-          for (int jj = 0; jj < NBW; ++jj) {
-            if (coff[jj] == kOOB) continue;
-            const int64_t e = (int64_t)grow * g.N + (coff[jj] >> 2);
-            int ap, an;
-            accs(fi, jj, r, ap, an);
-            g.dbg[e] = ap;
-            g.dbg[plane + e] = an;
-          }
-        }
-    }
+    if (g.dbg) dump_acc(m0, coff, jl);
     // Let the stores complete here, while no load is in flight: pending
     // stores would otherwise leave the compiler unable to account the loads
     // of the next steps, and it would drain the whole load stream later.
@@ -694,6 +782,18 @@ __device__ __forceinline__ void gemm_wave(const GemmArgs& g, int wave, int lane,
       zero_acc();
       cmp_k = 0;
       ++cmp_ti;
+      if constexpr (KS) {
+        cur_seg = 0;
+        seg_end = g.ks_end[0];
+      }
+    } else if constexpr (KS) {
+      if (cmp_k == seg_end) {
+        fold(cmp_ti);
+        zero_acc();
+        ++cur_seg;
+        // entries past the last branch hold a step count no tile reaches
+        seg_end = cur_seg == 1 ? g.ks_end[1] : cur_seg == 2 ? g.ks_end[2] : g.ks_end[3];
+      }
     }
   };
   int sb = 0;
@@ -708,7 +808,7 @@ __device__ __forceinline__ void gemm_wave(const GemmArgs& g, int wave, int lane,
   if (sb + 2 < total) step_epi(sb + 2, IC<2>{});
 }
 
-template <bool A4, bool SYM, bool CFG, bool HS, int NB>
+template <bool A4, bool SYM, bool CFG, bool HS, bool KS, int NB>
 __global__ __launch_bounds__(kThreads, 1) void k2_gemm(GemmArgs g) {
   using Lay = Layout<A4, NB>;
   // One LDS object per ring stage: the compiler tracks DMA -> LDS writes per
@@ -723,16 +823,16 @@ __global__ __launch_bounds__(kThreads, 1) void k2_gemm(GemmArgs g) {
   // waves w < NB - 8 also move weight pair w + 8 (NB is 8 or 9)
   static_assert(NB == 8 || NB == 9, "wave roles");
   if (wave < NB - 8)
-    gemm_wave<A4, SYM, CFG, HS, NB, 0, true>(g, wave, lane, st0, st1, st2, st3);
+    gemm_wave<A4, SYM, CFG, HS, KS, NB, 0, true>(g, wave, lane, st0, st1, st2, st3);
   else if (wave < 4)
-    gemm_wave<A4, SYM, CFG, HS, NB, 0, false>(g, wave, lane, st0, st1, st2, st3);
+    gemm_wave<A4, SYM, CFG, HS, KS, NB, 0, false>(g, wave, lane, st0, st1, st2, st3);
   else
-    gemm_wave<A4, SYM, CFG, HS, NB, 1, false>(g, wave, lane, st0, st1, st2, st3);
+    gemm_wave<A4, SYM, CFG, HS, KS, NB, 1, false>(g, wave, lane, st0, st1, st2, st3);
 }
 
 int g_cus = 0;  // compute units of the device (queried on first launch)
 
-template <bool A4, bool SYM, bool CFG, bool HS, int NB>
+template <bool A4, bool SYM, bool CFG, bool HS, bool KS, int NB>
 hipError_t run(const GemmArgs& g, hipStream_t s) {
   const int rpt = CFG ? 64 : 128;
   const int T = (((CFG ? g.Mh : g.M) + rpt - 1) / rpt) * ((g.N + 16 * NB - 1) / (16 * NB));
@@ -744,15 +844,15 @@ hipError_t run(const GemmArgs& g, hipStream_t s) {
     g_cus = cus;
   }
   const int G = T < g_cus ? T : g_cus;
-  hipLaunchKernelGGL((k2_gemm<A4, SYM, CFG, HS, NB>), dim3(G), dim3(kThreads), 0, s, g);
+  hipLaunchKernelGGL((k2_gemm<A4, SYM, CFG, HS, KS, NB>), dim3(G), dim3(kThreads), 0, s, g);
   return hipGetLastError();
 }
 
 template <bool A4, bool SYM, bool CFG>
 hipError_t run_nb(const GemmArgs& g, hipStream_t s) {
   // 144-column tiles when they divide N, else 128.
-  if (g.N % 144 == 0) return run<A4, SYM, CFG, false, 9>(g, s);
-  return run<A4, SYM, CFG, false, 8>(g, s);
+  if (g.N % 144 == 0) return run<A4, SYM, CFG, false, false, 9>(g, s);
+  return run<A4, SYM, CFG, false, false, 8>(g, s);
 }
 
 template <bool A4>
@@ -760,8 +860,17 @@ hipError_t run_mode(const GemmArgs& g, int sym, int cfg, int hs, hipStream_t s) 
   // Single Hadamard: symmetric codes, 128 weight rows (64 channels) per tile
   // so that every wave holds whole hi/lo pairs.
   if (hs) {
-    if (!sym) return hipErrorInvalidValue;
-    return cfg ? run<A4, true, true, true, 8>(g, s) : run<A4, true, false, true, 8>(g, s);
+    if (!sym || g.nks > 1) return hipErrorInvalidValue;
+    return cfg ? run<A4, true, true, true, false, 8>(g, s)
+               : run<A4, true, false, true, false, 8>(g, s);
+  }
+  // Input branches: 128-column tiles (the partial sums take 32 registers).
+  if (g.nks > 1) {
+    if (sym)
+      return cfg ? run<A4, true, true, false, true, 8>(g, s)
+                 : run<A4, true, false, false, true, 8>(g, s);
+    return cfg ? run<A4, false, true, false, true, 8>(g, s)
+               : run<A4, false, false, false, true, 8>(g, s);
   }
   if (sym) return cfg ? run_nb<A4, true, true>(g, s) : run_nb<A4, true, false>(g, s);
   return cfg ? run_nb<A4, false, true>(g, s) : run_nb<A4, false, false>(g, s);

@@ -37,12 +37,13 @@ __global__ __launch_bounds__(256) void k0_rotate(float* W, int64_t nunits) {
   if (idx < nunits) p[idx] = make_float4(e[0], e[1], e[2], e[3]);
 }
 
-// Bits of max_k |W[n,k]| per row (one block per row).
-__global__ __launch_bounds__(256) void k0_row_absmax(const float* W, int K, uint32_t* rowmax) {
+// Bits of max |W[n,k]| over the columns [c0, c0 + cw) per row (one block per row).
+__global__ __launch_bounds__(256) void k0_row_absmax(const float* W, int K, int c0, int cw,
+                                                     uint32_t* rowmax) {
   const int64_t n = blockIdx.x;
-  const float* row = W + n * K;
+  const float* row = W + n * K + c0;
   uint32_t m = 0;
-  for (int k = threadIdx.x; k < K; k += 256) {
+  for (int k = threadIdx.x; k < cw; k += 256) {
     const uint32_t b = __float_as_uint(row[k]) & 0x7FFFFFFFu;
     m = b > m ? b : m;
   }
@@ -82,20 +83,23 @@ __device__ __forceinline__ int quant_sym(float v, float s, float q) {
   return s > 0.0f ? (int)r : 0;
 }
 
-// Codes of 4 consecutive weights of one row per thread (K % 4 == 0), one
-// int8 per code for both widths (4-bit codes lie in [-7, 7]).
-__global__ __launch_bounds__(256) void k0_quant_w(const float* W, const float* sw, int K,
-                                                  int64_t nunits, float qw, uint8_t* out) {
+// Codes of 4 consecutive weights of one row per thread, over the columns
+// [c0, c0 + cw) of every row (K, c0, cw multiples of 4), one int8 per code
+// for both widths (4-bit codes lie in [-7, 7]).
+__global__ __launch_bounds__(256) void k0_quant_w(const float* W, const float* sw, int K, int c0,
+                                                  int cw, int64_t nunits, float qw,
+                                                  uint8_t* out) {
   const int64_t u = (int64_t)blockIdx.x * 256 + threadIdx.x;
   if (u >= nunits) return;
-  const int64_t n = (u * 4) / K;
+  const int64_t n = (u * 4) / cw;
+  const int64_t e = n * K + c0 + (u * 4 - n * cw);  // first element of the unit
   const float s = sw[n];
-  const float4 v = reinterpret_cast<const float4*>(W)[u];
-  const int c0 = quant_sym(v.x, s, qw), c1 = quant_sym(v.y, s, qw);
-  const int c2 = quant_sym(v.z, s, qw), c3 = quant_sym(v.w, s, qw);
-  reinterpret_cast<uint32_t*>(out)[u] =
-      (uint32_t)(c0 & 0xFF) | ((uint32_t)(c1 & 0xFF) << 8) | ((uint32_t)(c2 & 0xFF) << 16) |
-      ((uint32_t)(c3 & 0xFF) << 24);
+  const float4 v = *reinterpret_cast<const float4*>(W + e);
+  const int q0 = quant_sym(v.x, s, qw), q1 = quant_sym(v.y, s, qw);
+  const int q2 = quant_sym(v.z, s, qw), q3 = quant_sym(v.w, s, qw);
+  *reinterpret_cast<uint32_t*>(out + e) =
+      (uint32_t)(q0 & 0xFF) | ((uint32_t)(q1 & 0xFF) << 8) | ((uint32_t)(q2 & 0xFF) << 16) |
+      ((uint32_t)(q3 & 0xFF) << 24);
 }
 
 // TASQ on the weight side: clear the k low bits of every code's magnitude,
@@ -114,9 +118,9 @@ __device__ __forceinline__ uint32_t truncate4(uint32_t v, int32_t keep) {
 
 __global__ __launch_bounds__(256) void k0_truncate_w(const uint4* in, int64_t n16, int32_t keep,
                                                      uint4* out, const float* sw_in, float* sw_out,
-                                                     int N) {
+                                                     int nsw) {
   const int64_t u = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (u < N) sw_out[u] = sw_in[u];
+  if (u < nsw) sw_out[u] = sw_in[u];
   if (u >= n16) return;
   const uint4 v = in[u];
   out[u] = make_uint4(truncate4(v.x, keep), truncate4(v.y, keep), truncate4(v.z, keep),
@@ -189,8 +193,9 @@ hipError_t launch_rotate_rows(float* W, int64_t nunits, int hb, hipStream_t s) {
   return hipGetLastError();
 }
 
-hipError_t launch_row_absmax(const float* W, int N, int K, uint32_t* rowmax, hipStream_t s) {
-  hipLaunchKernelGGL(k0_row_absmax, dim3(N), dim3(256), 0, s, W, K, rowmax);
+hipError_t launch_row_absmax(const float* W, int N, int K, int c0, int cw, uint32_t* rowmax,
+                             hipStream_t s) {
+  hipLaunchKernelGGL(k0_row_absmax, dim3(N), dim3(256), 0, s, W, K, c0, cw, rowmax);
   return hipGetLastError();
 }
 
@@ -205,23 +210,24 @@ hipError_t launch_weight_scales(const uint32_t* rowmax, int N, int mode, const i
   return hipGetLastError();
 }
 
-hipError_t launch_quantize_weights(const float* W, const float* sw, int N, int K, float qw,
-                                   uint8_t* out, hipStream_t s) {
-  const int64_t nunits = (int64_t)N * K / 4;
-  hipLaunchKernelGGL(k0_quant_w, dim3(blocks_for(nunits, 256)), dim3(256), 0, s, W, sw, K, nunits,
-                     qw, out);
+hipError_t launch_quantize_weights(const float* W, const float* sw, int N, int K, int c0, int cw,
+                                   float qw, uint8_t* out, hipStream_t s) {
+  if (K % 4 || c0 % 4 || cw % 4 || cw <= 0 || c0 + cw > K) return hipErrorInvalidValue;
+  const int64_t nunits = (int64_t)N * cw / 4;
+  hipLaunchKernelGGL(k0_quant_w, dim3(blocks_for(nunits, 256)), dim3(256), 0, s, W, sw, K, c0, cw,
+                     nunits, qw, out);
   return hipGetLastError();
 }
 
 hipError_t launch_truncate_weights(const uint8_t* in, int64_t nbytes, int k, uint8_t* out,
-                                   const float* sw_in, float* sw_out, int N, hipStream_t s) {
+                                   const float* sw_in, float* sw_out, int nsw, hipStream_t s) {
   if (nbytes % 16 != 0 || k < 0 || k > 7) return hipErrorInvalidValue;
   const int64_t n16 = nbytes / 16;
   const int32_t keep = ~((1 << k) - 1);
-  const int64_t threads = n16 > N ? n16 : N;
+  const int64_t threads = n16 > nsw ? n16 : nsw;
   hipLaunchKernelGGL(k0_truncate_w, dim3(blocks_for(threads, 256)), dim3(256), 0, s,
                      reinterpret_cast<const uint4*>(in), n16, keep, reinterpret_cast<uint4*>(out),
-                     sw_in, sw_out, N);
+                     sw_in, sw_out, nsw);
   return hipGetLastError();
 }
 

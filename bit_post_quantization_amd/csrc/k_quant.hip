@@ -17,6 +17,11 @@
 // written, so there are two kernels: a max-reduction writing one partial
 // maximum pair per block (plain stores, no atomics), then the quantizer,
 // whose every block folds the partials into the scales first.
+//
+// With input branches (SegQuant explainer 2.A, input segmentation: a linear
+// fed by a concatenation quantizes each branch apart) the same two kernels
+// keep one maximum pair and one scale pair per branch; a unit's branch
+// follows from its column, tracked incrementally along the stream.
 #include "ql_device.h"
 #include "ql_kernels.h"
 
@@ -36,6 +41,22 @@ constexpr int kQuantBlocks = 2048;                // grid cap of the quantizer
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void* base, uint32_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes,
                                            0x00020000);
+}
+
+// Branch of a unit from its column in units (branch starts past the last
+// branch equal k_units, so they never match).
+__device__ __forceinline__ int branch_of(const QuantArgs& a, int c) {
+  return (c >= a.ks_units[1]) + (c >= a.ks_units[2]) + (c >= a.ks_units[3]);
+}
+
+// Column (in units) of this lane's first unit of a chunk, and the step to
+// the next unit of the lane (kThreads units further, modulo the row).
+__device__ __forceinline__ int first_col(const QuantArgs& a, int64_t first_unit) {
+  return (int)((first_unit + threadIdx.x) % a.k_units);
+}
+__device__ __forceinline__ int next_col(const QuantArgs& a, int c, int step) {
+  c += step;
+  return c >= a.k_units ? c - a.k_units : c;
 }
 
 // The kUnroll units of chunk `c` that this lane owns: unit c*kChunk + u*256 + tid.
@@ -69,32 +90,11 @@ __device__ __forceinline__ void load_chunk(const void* X, int64_t nunits, int64_
   }
 }
 
-template <bool BF16, int HB>
-__global__ __launch_bounds__(kThreads) void k1_reduce(QuantArgs a) {
+// Block-wide max of (mp, mn) into the partials of branch j.
+__device__ __forceinline__ void store_partials(const QuantArgs& a, int j, uint32_t mp,
+                                               uint32_t mn) {
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = threadIdx.x / kWave;
-  uint32_t mp = 0, mn = 0x80000000u;
-  const int64_t nchunks = (a.nunits + kChunk - 1) / kChunk;
-  for (int64_t c = blockIdx.x; c < nchunks; c += gridDim.x) {
-    float e[kUnroll][4];
-    load_chunk<BF16>(a.X, a.nunits, c, e);
-    if constexpr (HB > 0) {
-#pragma unroll
-      for (int u = 0; u < kUnroll; ++u) fwht_block<HB>(e[u], lane);
-    }
-    // On the bit patterns: non-negative floats order like their bits as
-    // signed integers (negative floats are negative integers), and negative
-    // floats order by magnitude like their bits as unsigned integers above
-    // 0x80000000 (non-negative floats lie below it). One integer max each.
-#pragma unroll
-    for (int u = 0; u < kUnroll; ++u)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const uint32_t b = __float_as_uint(e[u][i]);
-        mp = (uint32_t)max((int32_t)mp, (int32_t)b);
-        mn = max(mn, b);
-      }
-  }
   mn &= 0x7FFFFFFFu;  // magnitude of the most negative value (0 if none)
   mp = wave_max_u32(mp);
   mn = wave_max_u32(mn);
@@ -110,20 +110,68 @@ __global__ __launch_bounds__(kThreads) void k1_reduce(QuantArgs a) {
       mp = max(mp, sm[0][w]);
       mn = max(mn, sm[1][w]);
     }
-    a.ws->part[0][blockIdx.x] = mp;
-    a.ws->part[1][blockIdx.x] = mn;
+    a.ws->part[j][0][blockIdx.x] = mp;
+    a.ws->part[j][1][blockIdx.x] = mn;
   }
+  __syncthreads();  // sm is reused by the next branch
 }
 
-// Scales from the reduce kernel's per-block maxima (every block of the
-// quantize kernel does this; max is exact and order-free, so all agree).
-__device__ __forceinline__ void scales_from_partials(const QuantArgs& a, float& sp, float& sn) {
+template <bool BF16, int HB, bool KS>
+__global__ __launch_bounds__(kThreads) void k1_reduce(QuantArgs a) {
+  const int lane = threadIdx.x & (kWave - 1);
+  constexpr int NJ = KS ? kMaxKSeg : 1;
+  uint32_t mp[NJ], mn[NJ];
+#pragma unroll
+  for (int j = 0; j < NJ; ++j) {
+    mp[j] = 0;
+    mn[j] = 0x80000000u;
+  }
+  const int cstep = KS ? kThreads % a.k_units : 0;
+  const int64_t nchunks = (a.nunits + kChunk - 1) / kChunk;
+  for (int64_t c = blockIdx.x; c < nchunks; c += gridDim.x) {
+    float e[kUnroll][4];
+    load_chunk<BF16>(a.X, a.nunits, c, e);
+    if constexpr (HB > 0) {
+#pragma unroll
+      for (int u = 0; u < kUnroll; ++u) fwht_block<HB>(e[u], lane);
+    }
+    // On the bit patterns: non-negative floats order like their bits as
+    // signed integers (negative floats are negative integers), and negative
+    // floats order by magnitude like their bits as unsigned integers above
+    // 0x80000000 (non-negative floats lie below it). One integer max each.
+    // (Units past the end read as +0, which no maximum can lose to.)
+    int col = KS ? first_col(a, c * kChunk) : 0;
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      const int br = KS ? branch_of(a, col) : 0;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const uint32_t b = __float_as_uint(e[u][i]);
+#pragma unroll
+        for (int j = 0; j < NJ; ++j) {
+          const bool mine = !KS || br == j;
+          mp[j] = mine ? (uint32_t)max((int32_t)mp[j], (int32_t)b) : mp[j];
+          mn[j] = mine ? max(mn[j], b) : mn[j];
+        }
+      }
+      if constexpr (KS) col = next_col(a, col, cstep);
+    }
+  }
+#pragma unroll
+  for (int j = 0; j < NJ; ++j)
+    if (j < a.nks) store_partials(a, j, mp[j], mn[j]);
+}
+
+// Scales of branch j from the reduce kernel's per-block maxima (every block
+// of the quantize kernel does this; max is exact and order-free, so all agree).
+__device__ __forceinline__ void scales_from_partials(const QuantArgs& a, int j, float& sp,
+                                                     float& sn) {
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = threadIdx.x / kWave;
   uint32_t mp = 0, mn = 0;
   for (int i = threadIdx.x; i < a.reduce_blocks; i += kThreads) {
-    mp = max(mp, a.ws->part[0][i]);
-    mn = max(mn, a.ws->part[1][i]);
+    mp = max(mp, a.ws->part[j][0][i]);
+    mn = max(mn, a.ws->part[j][1][i]);
   }
   mp = wave_max_u32(mp);
   mn = wave_max_u32(mn);
@@ -138,6 +186,7 @@ __device__ __forceinline__ void scales_from_partials(const QuantArgs& a, float& 
     mp = max(mp, sm[0][w]);
     mn = max(mn, sm[1][w]);
   }
+  __syncthreads();  // sm is reused by the next branch
   const float mx = __uint_as_float(mp);
   const float mnv = __uint_as_float(mn);
   if (a.sym) {
@@ -176,22 +225,32 @@ __device__ __forceinline__ void quant_unit(const float (&e)[4], float sp, float 
   }
 }
 
-template <bool BF16, int HB, bool A4>
+template <bool BF16, int HB, bool A4, bool KS>
 __global__ __launch_bounds__(kThreads) void k1_quantize(QuantArgs a) {
   const int lane = threadIdx.x & (kWave - 1);
-  float sp, sn;
-  if (a.static_scales) {
-    sp = a.static_scales[0];
-    sn = a.static_scales[1];
-  } else {
-    scales_from_partials(a, sp, sn);
+  constexpr int NJ = KS ? kMaxKSeg : 1;
+  float sps[NJ], sns[NJ], rps[NJ], rns[NJ];
+#pragma unroll
+  for (int j = 0; j < NJ; ++j) {
+    float sp = 0.0f, sn = 0.0f;
+    if (j < a.nks) {
+      if (a.static_scales) {
+        sp = a.static_scales[2 * j];
+        sn = a.static_scales[2 * j + 1];
+      } else {
+        scales_from_partials(a, j, sp, sn);
+      }
+      if (blockIdx.x == 0 && threadIdx.x == 0) {
+        a.act_scales[2 * j] = sp;
+        a.act_scales[2 * j + 1] = sn;
+      }
+    }
+    sps[j] = sp;
+    sns[j] = sn;
+    rps[j] = sp > 0.0f ? 1.0f / sp : 0.0f;
+    rns[j] = sn > 0.0f ? 1.0f / sn : 0.0f;
   }
-  if (blockIdx.x == 0 && threadIdx.x == 0) {
-    a.act_scales[0] = sp;
-    a.act_scales[1] = sn;
-  }
-  const float rp = sp > 0.0f ? 1.0f / sp : 0.0f;
-  const float rn = sn > 0.0f ? 1.0f / sn : 0.0f;
+  const int cstep = KS ? kThreads % a.k_units : 0;
   constexpr uint32_t kCodeBytes = A4 ? 2 : 4;
   const int64_t nchunks = (a.nunits + kChunk - 1) / kChunk;
   for (int64_t ch = blockIdx.x; ch < nchunks; ch += gridDim.x) {
@@ -206,8 +265,21 @@ __global__ __launch_bounds__(kThreads) void k1_quantize(QuantArgs a) {
     const uint32_t here = (uint32_t)(left < kChunk ? left : kChunk);
     const __amdgpu_buffer_rsrc_t rc =
         buffer_rsrc(reinterpret_cast<uint8_t*>(a.codes) + first * kCodeBytes, here * kCodeBytes);
+    int col = KS ? first_col(a, first) : 0;
 #pragma unroll
     for (int u = 0; u < kUnroll; ++u) {
+      float sp = sps[0], sn = sns[0], rp = rps[0], rn = rns[0];
+      if constexpr (KS) {
+        const int br = branch_of(a, col);
+#pragma unroll
+        for (int j = 1; j < NJ; ++j) {
+          sp = br == j ? sps[j] : sp;
+          sn = br == j ? sns[j] : sn;
+          rp = br == j ? rps[j] : rp;
+          rn = br == j ? rns[j] : rn;
+        }
+        col = next_col(a, col, cstep);
+      }
       int c[4];
       quant_unit(e[u], sp, sn, rp, rn, a.qa, c);
       if (a.keep_mask != -1) {
@@ -240,18 +312,25 @@ int balanced_grid(int nch, int cap) {
   return (nch + per - 1) / per;
 }
 
-template <bool BF16, int HB, bool A4>
-hipError_t run(QuantArgs a, hipStream_t s) {
+template <bool BF16, int HB, bool A4, bool KS>
+hipError_t run_ks(QuantArgs a, hipStream_t s) {
   const int nch = chunks_of(a.nunits);
   const int g = balanced_grid(nch, kQuantBlocks);
   if (!a.static_scales) {
     a.reduce_blocks = balanced_grid(nch, kMaxReduceBlocks);
-    hipLaunchKernelGGL((k1_reduce<BF16, HB>), dim3(a.reduce_blocks), dim3(kThreads), 0, s, a);
+    hipLaunchKernelGGL((k1_reduce<BF16, HB, KS>), dim3(a.reduce_blocks), dim3(kThreads), 0, s,
+                       a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  hipLaunchKernelGGL((k1_quantize<BF16, HB, A4>), dim3(g), dim3(kThreads), 0, s, a);
+  hipLaunchKernelGGL((k1_quantize<BF16, HB, A4, KS>), dim3(g), dim3(kThreads), 0, s, a);
   return hipGetLastError();
+}
+
+template <bool BF16, int HB, bool A4>
+hipError_t run(const QuantArgs& a, hipStream_t s) {
+  if (a.nks > 1) return run_ks<BF16, HB, A4, true>(a, s);
+  return run_ks<BF16, HB, A4, false>(a, s);
 }
 
 template <bool BF16, bool A4>

@@ -10,28 +10,33 @@ namespace ql {
 // max-reduce kernel and read by the quantize kernel of the same call (stream
 // order makes them visible; nothing needs clearing between calls).
 constexpr int kMaxReduceBlocks = 1024;
+constexpr int kMaxKSeg = 4;  // input branches (SegLinear input segmentation)
 struct ReduceWs {
-  uint32_t part[2][kMaxReduceBlocks];  // bits of max(+0, max x), max(+0, -min x)
+  // per branch: bits of max(+0, max x), max(+0, -min x)
+  uint32_t part[kMaxKSeg][2][kMaxReduceBlocks];
 };
 
 struct QuantArgs {
   const void* X;
   int64_t nunits;            // number of 4-element units (M*K/4)
   void* codes;
-  float* act_scales;         // out [2]
-  const float* static_scales;// in [2] or nullptr
+  float* act_scales;         // out [2 * nks]
+  const float* static_scales;// in [2 * nks] or nullptr
   ReduceWs* ws;
   int reduce_blocks;         // partials written by the reduce kernel
   float qa;
   int keep_mask;             // ~((1 << lsb_k) - 1)
   int sym;
+  int nks;                   // input branches (1: one scale pair for the tensor)
+  int k_units;               // K / 4
+  int ks_units[kMaxKSeg];    // branch starts in units (k_j / 4); unused ones = k_units
 };
 
 struct GemmArgs {
   const uint8_t* A;          // activation codes: int8 [M,K] or packed [M,K/2]
   const uint8_t* W;          // weight codes: int8 [N,K] (4-bit codes expanded)
-  const float* act_scales;   // [2]
-  const float* w_scales;     // [N]
+  const float* act_scales;   // [2 * nks]
+  const float* w_scales;     // [nks * Nout]
   float* Y;                  // [M,N] or [M/2,N]
   int32_t* dbg;              // [2,M,N] or nullptr
   int M, N, K;               // N: weight rows (2 * roundup(Nout, 16) for single Hadamard)
@@ -40,12 +45,25 @@ struct GemmArgs {
   int64_t lda, ldw;          // bytes per row of A / W
   float guidance;
   float inv_b;               // 1/B (rotation) or 1
+  int nks;                   // input branches (1: none)
+  int ks_end[kMaxKSeg];      // K-step (of 128) at which each branch but the last ends
+  float* ypart_ws;           // input branches: kYSlots * kGemmThreads floats per workgroup
 };
+
+// GEMM workgroup size and the per-thread partial-sum slots of a GEMM with
+// input branches; the workspace holds one block per workgroup (at most one
+// workgroup per compute unit).
+constexpr int kGemmThreads = 512;
+constexpr int kYSlots = 32;
+inline size_t gemm_ypart_bytes(int cus) {
+  return (size_t)cus * kYSlots * kGemmThreads * sizeof(float);
+}
 
 // K1: activation quantization. Returns the launch status.
 hipError_t launch_quantize(const QuantArgs& a, int x_bf16, int hadamard_block, int a4,
                            hipStream_t s);
 
+// K1 with input branches: launch_quantize handles a.nks > 1 too.
 // K2: GEMM + epilogue.
 // hs: single-Hadamard weight planes (requires sym).
 hipError_t launch_gemm(const GemmArgs& g, int a4, int sym, int cfg, int hs, hipStream_t s);
@@ -56,19 +74,22 @@ hipError_t launch_cfg_combine(const float* Y, int64_t half_elems, float w, float
 
 // K0: plan kernels.
 hipError_t launch_rotate_rows(float* W, int64_t nunits, int hadamard_block, hipStream_t s);
-hipError_t launch_row_absmax(const float* W, int N, int K, uint32_t* rowmax, hipStream_t s);
+// Max |W[n, c0 .. c0+cw)| per row (row stride K).
+hipError_t launch_row_absmax(const float* W, int N, int K, int c0, int cw, uint32_t* rowmax,
+                             hipStream_t s);
 hipError_t launch_weight_scales(const uint32_t* rowmax, int N, int mode, const int32_t* seg,
                                 int nseg, float qw, float* sw, hipStream_t s);
-hipError_t launch_quantize_weights(const float* W, const float* sw, int N, int K, float qw,
-                                   uint8_t* out, hipStream_t s);
+// Codes of the columns [c0, c0 + cw) of W (row stride K) with the scales sw[N].
+hipError_t launch_quantize_weights(const float* W, const float* sw, int N, int K, int c0, int cw,
+                                   float qw, uint8_t* out, hipStream_t s);
 // Single-Hadamard weight planes: out has 2 * roundup(N, 16) rows of K bytes
 // (hi / lo interleaved per 16 channels; rows past N must be zeroed by the
 // caller). K % 4 == 0 and K % hadamard_block == 0.
 hipError_t launch_fwht_split(const uint8_t* codes, int N, int K, int hadamard_block, uint8_t* out,
                              hipStream_t s);
 // Weight codes with the k low magnitude bits cleared (nbytes % 16 == 0,
-// 16-byte aligned), and a copy of the N weight scales.
+// 16-byte aligned), and a copy of the nsw weight scales.
 hipError_t launch_truncate_weights(const uint8_t* in, int64_t nbytes, int k, uint8_t* out,
-                                   const float* sw_in, float* sw_out, int N, hipStream_t s);
+                                   const float* sw_in, float* sw_out, int nsw, hipStream_t s);
 
 }  // namespace ql

@@ -15,10 +15,13 @@
 struct qlinear_plan {
   ql_desc d;
   std::vector<int32_t> seg;  // host copy, n_segments + 1
+  std::vector<int32_t> kseg; // input branch offsets, nks + 1 ({0, K} without branches)
+  int nks = 1;
   int device = -1;
   uint8_t* wq = nullptr;     // GEMM weights: codes int8 [N,K], or the two planes of
                              // H W_int^T, int8 [2 * roundup(N,16), K] (single Hadamard)
   uint8_t* wint = nullptr;   // single Hadamard: the codes W_int, int8 [N,K]
+  float* ypart = nullptr;    // input branches: the GEMM's partial-sum workspace
   float* sw = nullptr;       // weight scales [N]
   ql::ReduceWs* ws = nullptr;
 };
@@ -83,6 +86,25 @@ ql_status check_desc(const ql_desc* d) {
     return fail(QL_ERR_ARG, "single_hadamard needs hadamard_block > 0");
   if (d->single_hadamard && d->a_scale_mode != QL_ASCALE_SYMMETRIC)
     return fail(QL_ERR_UNSUPPORTED, "single_hadamard supports SYMMETRIC activation scales only");
+  if (d->n_k_segments < 0)
+    return fail(QL_ERR_ARG, "n_k_segments = %d must be >= 0", d->n_k_segments);
+  if (d->n_k_segments > 1) {
+    const int S = d->n_k_segments;
+    if (S > ql::kMaxKSeg)
+      return fail(QL_ERR_UNSUPPORTED, "n_k_segments = %d: at most %d input branches", S,
+                  ql::kMaxKSeg);
+    if (!d->k_seg_offsets) return fail(QL_ERR_ARG, "k_seg_offsets is NULL with n_k_segments = %d", S);
+    const int32_t* o = d->k_seg_offsets;
+    if (o[0] != 0 || o[S] != d->K)
+      return fail(QL_ERR_ARG, "input branches must start at 0 and end at K = %d", d->K);
+    for (int j = 0; j < S; ++j)
+      if (o[j + 1] <= o[j]) return fail(QL_ERR_ARG, "input branch %d is empty or descending", j);
+    for (int j = 1; j < S; ++j)
+      if (o[j] % 128 != 0)
+        return fail(QL_ERR_UNSUPPORTED, "input branch offset %d is not a multiple of 128", o[j]);
+    if (d->single_hadamard)
+      return fail(QL_ERR_UNSUPPORTED, "single_hadamard with input branches");
+  }
   if (d->n_segments < 1) return fail(QL_ERR_ARG, "n_segments = %d must be >= 1", d->n_segments);
   if (d->n_segments > 1 && !d->seg_offsets)
     return fail(QL_ERR_ARG, "seg_offsets is NULL with n_segments = %d", d->n_segments);
@@ -94,6 +116,16 @@ ql_status check_desc(const ql_desc* d) {
       if (o[g + 1] <= o[g]) return fail(QL_ERR_ARG, "segment %d is empty or descending", g);
   }
   return QL_OK;
+}
+
+// Partial-sum workspace of the GEMM for plans with input branches (one
+// block per compute unit of the device).
+hipError_t alloc_ypart(struct qlinear_plan* p) {
+  if (p->nks <= 1) return hipSuccess;
+  int cus = 0;
+  hipError_t e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, p->device);
+  if (e != hipSuccess) return e;
+  return hipMalloc(&p->ypart, ql::gemm_ypart_bytes(cus));
 }
 
 // Rows of the weight matrix the GEMM reads: N, or the hi/lo planes of every
@@ -116,6 +148,7 @@ void free_plan(struct qlinear_plan* p) {
   if (p->wq) (void)hipFree(p->wq);
   if (p->sw) (void)hipFree(p->sw);
   if (p->wint) (void)hipFree(p->wint);
+  if (p->ypart) (void)hipFree(p->ypart);
   if (p->ws) (void)hipFree(p->ws);
   delete p;
 }
@@ -128,7 +161,7 @@ bool same_layer(const struct qlinear_plan* a, const struct qlinear_plan* b) {
          x.hadamard_block == y.hadamard_block && x.n_segments == y.n_segments &&
          x.w_scale_mode == y.w_scale_mode && x.a_scale_mode == y.a_scale_mode &&
          x.x_dtype == y.x_dtype && x.single_hadamard == y.single_hadamard && a->seg == b->seg &&
-         a->device == b->device;
+         a->kseg == b->kseg && a->device == b->device;
 }
 
 // Enqueue view's weights = base's codes with k low magnitude bits cleared,
@@ -139,7 +172,7 @@ ql_status enqueue_lsb(struct qlinear_plan* view, const struct qlinear_plan* base
   const bool single = base->d.single_hadamard != 0;
   hipError_t e = ql::launch_truncate_weights(single ? base->wint : base->wq, nbytes, k,
                                              single ? view->wint : view->wq, base->sw, view->sw,
-                                             base->d.N, s);
+                                             base->nks * base->d.N, s);
   if (e != hipSuccess) return hip_fail(e, "truncating weight codes");
   if (single) {  // rebuild the hi/lo planes from the truncated codes
     e = ql::launch_fwht_split(view->wint, base->d.N, base->d.K, base->d.hadamard_block, view->wq,
@@ -180,6 +213,14 @@ ql_status qlinear_plan(const ql_desc* d, const float* W, void* stream, qlinear_p
     p->d.n_segments = 1;
   }
   p->d.seg_offsets = nullptr;
+  if (d->n_k_segments > 1) {
+    p->kseg.assign(d->k_seg_offsets, d->k_seg_offsets + d->n_k_segments + 1);
+  } else {
+    p->kseg = {0, d->K};
+    p->d.n_k_segments = 1;
+  }
+  p->nks = (int)p->kseg.size() - 1;
+  p->d.k_seg_offsets = nullptr;
   if (hipGetDevice(&p->device) != hipSuccess) {
     free_plan(p);
     return fail(QL_ERR_HIP, "hipGetDevice failed");
@@ -210,9 +251,10 @@ ql_status qlinear_plan(const ql_desc* d, const float* W, void* stream, qlinear_p
   } while (0)
   QL_TRY(hipMalloc(&p->wq, gbytes), "allocating weight codes");
   if (single) QL_TRY(hipMalloc(&p->wint, wbytes), "allocating unrotated weight codes");
-  QL_TRY(hipMalloc(&p->sw, N * sizeof(float)), "allocating weight scales");
+  QL_TRY(hipMalloc(&p->sw, (size_t)p->nks * N * sizeof(float)), "allocating weight scales");
   QL_TRY(hipMalloc(&p->ws, sizeof(ql::ReduceWs)), "allocating reduction workspace");
   QL_TRY(hipMalloc(&rowmax, N * sizeof(uint32_t)), "allocating row maxima");
+  QL_TRY(alloc_ypart(p), "allocating partial-sum workspace");
   // Offsets that define the scale groups: the given segments for
   // PER_SEGMENT, one group [0,N) for PER_TENSOR (unused for PER_CHANNEL).
   const int mode = d->w_scale_mode == QL_WSCALE_PER_SEGMENT  ? 1
@@ -234,11 +276,18 @@ ql_status qlinear_plan(const ql_desc* d, const float* W, void* stream, qlinear_p
     src = rot;
   }
   const float qw = (float)qmax(d->w_bits);
-  QL_TRY(ql::launch_row_absmax(src, (int)N, (int)K, rowmax, s), "weight row maxima");
-  QL_TRY(ql::launch_weight_scales(rowmax, (int)N, mode, segd, ngroups, qw, p->sw, s),
-         "weight scales");
-  QL_TRY(ql::launch_quantize_weights(src, p->sw, (int)N, (int)K, qw, single ? p->wint : p->wq, s),
-         "weight codes");
+  // Every input branch (the whole row without branches) has its own scales
+  // over its own columns.
+  for (int j = 0; j < p->nks; ++j) {
+    const int c0 = p->kseg[j], cw = p->kseg[j + 1] - p->kseg[j];
+    float* swj = p->sw + (int64_t)j * N;
+    QL_TRY(ql::launch_row_absmax(src, (int)N, (int)K, c0, cw, rowmax, s), "weight row maxima");
+    QL_TRY(ql::launch_weight_scales(rowmax, (int)N, mode, segd, ngroups, qw, swj, s),
+           "weight scales");
+    QL_TRY(ql::launch_quantize_weights(src, swj, (int)N, (int)K, c0, cw, qw,
+                                       single ? p->wint : p->wq, s),
+           "weight codes");
+  }
   if (single) {
     QL_TRY(hipMemsetAsync(p->wq, 0, gbytes, s), "clearing weight planes");
     QL_TRY(ql::launch_fwht_split(p->wint, (int)N, (int)K, d->hadamard_block, p->wq, s),
@@ -267,12 +316,15 @@ ql_status qlinear_plan_lsb_view(qlinear_plan_t base, int32_t w_lsb_k, void* stre
   auto* v = new struct qlinear_plan();
   v->d = base->d;
   v->seg = base->seg;
+  v->kseg = base->kseg;
+  v->nks = base->nks;
   v->device = base->device;
   const size_t wbytes = (size_t)base->d.N * base->d.K;
   const size_t gbytes = gemm_weight_rows(base->d) * (size_t)base->d.K;
   hipError_t e = hipMalloc(&v->wq, gbytes);
-  if (e == hipSuccess) e = hipMalloc(&v->sw, (size_t)base->d.N * sizeof(float));
+  if (e == hipSuccess) e = hipMalloc(&v->sw, (size_t)base->nks * base->d.N * sizeof(float));
   if (e == hipSuccess) e = hipMalloc(&v->ws, sizeof(ql::ReduceWs));
+  if (e == hipSuccess) e = alloc_ypart(v);
   if (e == hipSuccess && base->d.single_hadamard) {
     e = hipMalloc(&v->wint, wbytes);
     // rows past N of the planes stay zero for the life of the view
@@ -324,7 +376,8 @@ ql_status qlinear_plan_weights(qlinear_plan_t p, int8_t* w_codes, float* w_scale
     if (e != hipSuccess) return hip_fail(e, "copying weight codes");
   }
   if (w_scales) {
-    e = hipMemcpyAsync(w_scales, p->sw, (size_t)p->d.N * sizeof(float), hipMemcpyDeviceToDevice, s);
+    e = hipMemcpyAsync(w_scales, p->sw, (size_t)p->nks * p->d.N * sizeof(float),
+                       hipMemcpyDeviceToDevice, s);
     if (e != hipSuccess) return hip_fail(e, "copying weight scales");
   }
   return ok();
@@ -356,6 +409,9 @@ ql_status qlinear_quantize_act(qlinear_plan_t p, const void* X, int32_t M, int32
   a.qa = (float)qmax(p->d.a_bits);
   a.keep_mask = ~((1 << lsb_k) - 1);
   a.sym = p->d.a_scale_mode == QL_ASCALE_SYMMETRIC;
+  a.nks = p->nks;
+  a.k_units = p->d.K / 4;
+  for (int j = 0; j < ql::kMaxKSeg; ++j) a.ks_units[j] = j < p->nks ? p->kseg[j] / 4 : a.k_units;
   hipError_t e = ql::launch_quantize(a, bf16, p->d.hadamard_block, p->d.a_bits == 4,
                                      reinterpret_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "launching quantize");
@@ -393,6 +449,10 @@ ql_status qlinear_gemm(qlinear_plan_t p, const void* codes, const float* act_sca
     return fail(QL_ERR_UNSUPPORTED, "codes or weights of 2 GiB or more (M = %d)", M);
   g.guidance = w;
   g.inv_b = p->d.hadamard_block ? 1.0f / (float)p->d.hadamard_block : 1.0f;
+  g.nks = p->nks;
+  g.ypart_ws = p->ypart;
+  for (int j = 0; j < ql::kMaxKSeg; ++j)
+    g.ks_end[j] = j + 1 < p->nks ? p->kseg[j + 1] / 128 : 0x7FFFFFFF;
   hipError_t e = ql::launch_gemm(g, p->d.a_bits == 4,
                                  p->d.a_scale_mode == QL_ASCALE_SYMMETRIC, cfg,
                                  p->d.single_hadamard,

@@ -58,24 +58,33 @@ class Plan:
 def qlinear_plan(W, N: int, K: int, w_bits: int = 8, a_bits: int = 8, hadamard_block: int = 0,
                  seg_offsets: Optional[Sequence[int]] = None, w_scale: str = "channel",
                  a_scale: str = "dual", x_dtype: str = "f32", stream=None,
-                 single_hadamard: bool = False) -> Plan:
+                 single_hadamard: bool = False,
+                 k_seg_offsets: Optional[Sequence[int]] = None) -> Plan:
     L = _lib.load()
     segs = None
     nseg = 1
     if seg_offsets is not None:
         nseg = len(seg_offsets) - 1
         segs = (ctypes.c_int32 * len(seg_offsets))(*[int(v) for v in seg_offsets])
+    ksegs = None
+    nks = 0
+    if k_seg_offsets is not None:
+        nks = len(k_seg_offsets) - 1
+        ksegs = (ctypes.c_int32 * len(k_seg_offsets))(*[int(v) for v in k_seg_offsets])
     d = QlDesc(N=N, K=K, w_bits=w_bits, a_bits=a_bits, hadamard_block=hadamard_block,
                n_segments=nseg,
                seg_offsets=ctypes.cast(segs, ctypes.POINTER(ctypes.c_int32)) if segs else None,
                w_scale_mode=_WMODES[w_scale], a_scale_mode=_AMODES[a_scale],
-               x_dtype=_DTYPES[x_dtype], single_hadamard=int(bool(single_hadamard)))
+               x_dtype=_DTYPES[x_dtype], single_hadamard=int(bool(single_hadamard)),
+               n_k_segments=nks,
+               k_seg_offsets=ctypes.cast(ksegs, ctypes.POINTER(ctypes.c_int32)) if ksegs else None)
     h = ctypes.c_void_p()
     check(L.qlinear_plan(ctypes.byref(d), _ptr(W), _stream(stream), ctypes.byref(h)))
     return Plan(h.value, dict(N=N, K=K, w_bits=w_bits, a_bits=a_bits,
                               hadamard_block=hadamard_block, seg_offsets=seg_offsets,
                               w_scale=w_scale, a_scale=a_scale, x_dtype=x_dtype,
-                              single_hadamard=bool(single_hadamard)))
+                              single_hadamard=bool(single_hadamard),
+                              k_seg_offsets=k_seg_offsets))
 
 
 def qlinear_plan_destroy(plan: Plan) -> None:
@@ -139,19 +148,21 @@ class QuantLinear:
 
     def __init__(self, W, w_bits=8, a_bits=8, hadamard_block=0, seg_offsets=None,
                  w_scale="channel", a_scale="dual", x_dtype="f32", stream=None,
-                 single_hadamard=False):
+                 single_hadamard=False, k_seg_offsets=None):
         N, K = W.shape
         self.N, self.K = int(N), int(K)
         self.a_bits, self.w_bits = a_bits, w_bits
+        self.nks = 1 if k_seg_offsets is None else len(k_seg_offsets) - 1
         self.plan = qlinear_plan(W, self.N, self.K, w_bits, a_bits, hadamard_block, seg_offsets,
-                                 w_scale, a_scale, x_dtype, stream, single_hadamard)
+                                 w_scale, a_scale, x_dtype, stream, single_hadamard,
+                                 k_seg_offsets)
         self.base = None
 
     def lsb_view(self, w_lsb_k: int, stream=None) -> "QuantLinear":
         """The same layer run with w_lsb_k low bits of every weight code
         dropped; ``update_lsb`` changes the depth later without allocating."""
         v = QuantLinear.__new__(QuantLinear)
-        v.N, v.K, v.a_bits, v.w_bits = self.N, self.K, self.a_bits, self.w_bits
+        v.N, v.K, v.a_bits, v.w_bits, v.nks = self.N, self.K, self.a_bits, self.w_bits, self.nks
         v.plan = qlinear_plan_lsb_view(self.plan, w_lsb_k, stream)
         v.base = self
         return v
@@ -171,7 +182,7 @@ class QuantLinear:
         import torch
         M = X.shape[0]
         codes = self.alloc_codes(M) if codes is None else codes
-        act_scales = (torch.empty(2, dtype=torch.float32, device="cuda")
+        act_scales = (torch.empty(2 * self.nks, dtype=torch.float32, device="cuda")
                       if act_scales is None else act_scales)
         qlinear_quantize_act(self.plan, X, M, lsb_k, static_scales, codes, act_scales, stream)
         return codes, act_scales
@@ -191,6 +202,6 @@ class QuantLinear:
     def weights(self, stream=None):
         import torch
         wc = torch.empty((self.N, self.K), dtype=torch.int8, device="cuda")
-        sw = torch.empty(self.N, dtype=torch.float32, device="cuda")
+        sw = torch.empty(self.N * self.nks, dtype=torch.float32, device="cuda")
         qlinear_plan_weights(self.plan, wc, sw, stream)
-        return wc, sw
+        return wc, (sw.view(self.nks, self.N) if self.nks > 1 else sw)

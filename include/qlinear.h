@@ -36,9 +36,11 @@
  *     thread).
  *   - Inputs must be finite; non-finite values give unspecified codes.
  *   - A plan is immutable after qlinear_plan returns, except for a small
- *     internal reduction workspace used by qlinear_quantize_act: calls of
+ *     internal reduction workspace used by qlinear_quantize_act and, with
+ *     input branches, a partial-sum workspace used by qlinear_gemm: calls of
  *     qlinear_quantize_act with dynamic scales on one plan must be ordered
- *     (one stream, or explicit events); other calls may run concurrently.
+ *     (one stream, or explicit events), and so must calls of qlinear_gemm on
+ *     one plan with input branches; other calls may run concurrently.
  */
 #ifndef QLINEAR_H
 #define QLINEAR_H
@@ -89,6 +91,12 @@ typedef struct {
                                 quantized unrotated and enters the product as
                                 H W_int^T. Needs hadamard_block > 0 and
                                 a_scale_mode SYMMETRIC (HQ-DM explainer 2.2). */
+  int32_t n_k_segments;      /* input branches S (SegQuant explainer 2.A, input
+                                segmentation: the input is a concatenation along
+                                K and each branch is quantized on its own):
+                                0 or 1 = none, at most 4 */
+  const int32_t* k_seg_offsets;/* HOST [S+1]: 0 = k_0 < k_1 < ... < k_S = K, the
+                                inner ones multiples of 128; NULL when S <= 1 */
 } ql_desc;
 
 /* Shape rules checked by every call: K % 16 == 0 when both w_bits and
@@ -100,16 +108,20 @@ typedef struct {
  * butterfly distance 1, 2, ..., B/2, each (a,b) -> (a+b, a-b) in fp32), take
  * the symmetric absmax weight scale per channel / segment / tensor
  * (s = absmax / qmax_w, qmax_w = 2^(w_bits-1) - 1), quantize
- * (round half to even, clamp to [-qmax_w, qmax_w]). The plan keeps one
+ * (round half to even, clamp to [-qmax_w, qmax_w]); with input branches,
+ * each branch's columns get their own scales, s_w[j][n], by the same rule
+ * over those columns only. The plan keeps one
  * signed byte per weight code for both widths (4-bit codes lie in [-7, 7]):
  * the GEMM is bound by its matrix-core and vector issue, not by weight bytes,
  * so it reads 4-bit weights without an unpack step.
- *   d   : HOST descriptor (copied; seg_offsets copied too).
+ *   d   : HOST descriptor (copied; seg_offsets and k_seg_offsets copied too).
  *   W   : DEVICE fp32 [N,K]; read only, may be freed after the call.
  *   out : HOST; receives the plan handle.
  * Allocates device memory for the plan and synchronises `stream` before it
  * returns (plan building is offline work). Errors: QL_ERR_ARG for a bad
- * descriptor or NULL pointer, QL_ERR_OOM, QL_ERR_HIP.
+ * descriptor or NULL pointer, QL_ERR_UNSUPPORTED for more than 4 input
+ * branches, an inner branch offset that is not a multiple of 128, or input
+ * branches with single_hadamard, QL_ERR_OOM, QL_ERR_HIP.
  */
 ql_status qlinear_plan(const ql_desc* d, const float* W, void* stream, qlinear_plan_t* out);
 /* With single_hadamard = 1 the plan quantizes W without rotation (scales and
@@ -125,7 +137,8 @@ ql_status qlinear_plan_destroy(qlinear_plan_t p);
 
 /* Copy a plan's weights out for inspection: w_codes DEVICE int8 [N,K]
  * (one code per byte; the unrotated W_int for single_hadamard), w_scales
- * DEVICE fp32 [N]. Either may be NULL to skip it. */
+ * DEVICE fp32 [S,N] (S input branches, 1 without). Either may be NULL to
+ * skip it. */
 ql_status qlinear_plan_weights(qlinear_plan_t p, int8_t* w_codes, float* w_scales, void* stream);
 
 /*
@@ -173,14 +186,18 @@ ql_status qlinear_plan_lsb_update(qlinear_plan_t view, qlinear_plan_t base, int3
  * round_half_even(x / s-) clamped to [-qa, 0] (a zero scale gives 0;
  * division is IEEE fp32, correctly rounded); then, when lsb_k > 0, the k low
  * bits of the code's magnitude are cleared with the sign kept.
+ * With S > 1 input branches every branch (the columns [k_j, k_j+1) of all
+ * rows) gets its own scale pair, taken and applied as above over its values
+ * only.
  *   X             : DEVICE [M,K], fp32 or bf16 per the plan.
  *   M             : rows, >= 0 (0 enqueues nothing).
  *   lsb_k         : 0 <= lsb_k < a_bits.
- *   static_scales : DEVICE fp32 [2] {s+, s-}, or NULL for dynamic scales.
+ *   static_scales : DEVICE fp32 [2S] {s+, s-} per branch, or NULL for
+ *                   dynamic scales (S = 1 without input branches).
  *   codes         : DEVICE out: int8 [M,K] (a_bits 8) or uint8 [M,K/2]
  *                   (a_bits 4), two 4-bit two's-complement codes per byte:
  *                   element 2j in bits 0-3 and 2j+1 in bits 4-7 of byte j.
- *   act_scales    : DEVICE out fp32 [2] {s+, s-} used for the codes.
+ *   act_scales    : DEVICE out fp32 [2S] {s+, s-} per branch, as used.
  */
 ql_status qlinear_quantize_act(qlinear_plan_t p, const void* X, int32_t M, int32_t lsb_k,
                                const float* static_scales, void* codes, float* act_scales,
@@ -191,10 +208,13 @@ ql_status qlinear_quantize_act(qlinear_plan_t p, const void* X, int32_t M, int32
  * epilogue. DUAL: acc+ = sum_k max(c,0) w, acc- = sum_k min(c,0) w (int32,
  * exact), y = ((float)acc+ * s+ + (float)acc- * s-) * s_w[n];
  * SYMMETRIC: y = ((float)(acc+ + acc-) * s) * s_w[n]; then y *= 1/B when the
- * plan rotates (B = hadamard_block). All fp32 operations are rounded
+ * plan rotates (B = hadamard_block). With S > 1 input branches, y_j is the
+ * above (before 1/B) over branch j's columns with its own scales s_j and
+ * weight scales s_w[j][n], and y = (((y_0 + y_1) + y_2) + ...) * (1/B).
+ * All fp32 operations are rounded
  * individually in this order (no fused multiply-add).
  *   codes      : DEVICE, as written by qlinear_quantize_act, M rows.
- *   act_scales : DEVICE fp32 [2].
+ *   act_scales : DEVICE fp32 [2S].
  *   M          : rows, >= 0; must be even when cfg = 1.
  *   cfg        : 0 -> Y [M,N] = y.
  *                1 -> rows [0,M/2) are conditional, [M/2,M) unconditional;
@@ -202,8 +222,8 @@ ql_status qlinear_quantize_act(qlinear_plan_t p, const void* X, int32_t M, int32
  *                     t = w * d, Y = yu + t rounded in that order.
  *   w          : guidance weight (used when cfg = 1).
  *   Y          : DEVICE fp32 out, [M,N] or [M/2,N].
- *   acc_dbg    : NULL, or DEVICE int32 [2,M,N] out: plane 0 = acc+, plane
- *                1 = acc- for every row (SYMMETRIC: plane 0 = acc+ + acc-,
+ *   acc_dbg    : NULL, or DEVICE int32 [2S,M,N] out: plane 2j = acc+, plane
+ *                2j+1 = acc- of branch j for every row (SYMMETRIC: plane 0 = acc+ + acc-,
  *                plane 1 = 0; single_hadamard: the exact sum is 128 * plane 0
  *                + plane 1, the products with the hi and lo planes). For
  *                parity checks; costs extra stores.

@@ -54,6 +54,24 @@ def compare_codes(gpu: np.ndarray, ref: np.ndarray, x_rot: np.ndarray, s: np.nda
     return dict(n=int(gpu.size), mismatched=int(mism.size), flagged=flagged, unflagged=unflagged)
 
 
+def compare_codes_scaled(gpu: np.ndarray, ref: np.ndarray, x_rot: np.ndarray,
+                         s_el: np.ndarray) -> dict:
+    """As compare_codes, with a scale pair per element: s_el [M, K, 2]."""
+    gpu = gpu.reshape(-1)
+    ref = ref.reshape(-1)
+    mism = np.nonzero(gpu != ref)[0]
+    flagged = unflagged = 0
+    if mism.size:
+        x = x_rot.reshape(-1)[mism].astype(np.float64)
+        se = s_el.reshape(-1, 2)[mism]
+        sel = np.where(x >= 0, se[:, 0], se[:, 1]).astype(np.float64)
+        v = x / sel
+        near = np.abs(v - (np.floor(v) + 0.5)) <= CODE_FLAG_REL * np.abs(v)
+        flagged = int(near.sum())
+        unflagged = int((~near).sum())
+    return dict(n=int(gpu.size), mismatched=int(mism.size), flagged=flagged, unflagged=unflagged)
+
+
 def assert_codes(stats: dict, what: str = "codes"):
     assert stats["unflagged"] == 0, f"{what}: {stats}"
     assert stats["flagged"] <= CODE_FLAG_FRAC * stats["n"], f"{what}: {stats}"

@@ -119,3 +119,21 @@ def test_cfg_combine_host_checks():
     assert "overlaps" in L.qlinear_last_error().decode()
     # empty input is a no-op and never reaches a launch
     assert L.qlinear_cfg_combine(0x1000, 0, 4, 4.0, 0x9000, None) == _lib.QL_OK
+
+
+def test_plan_rejects_bad_input_branches():
+    def st(offs, **kw):
+        arr = (ctypes.c_int32 * len(offs))(*offs)
+        d = _desc(K=512, n_k_segments=len(offs) - 1,
+                  k_seg_offsets=ctypes.cast(arr, ctypes.POINTER(ctypes.c_int32)), **kw)
+        return _plan_status(d)
+    assert st([0, 256, 512], hadamard_block=128, a_scale_mode=1, single_hadamard=1)[0] == \
+        _lib.QL_ERR_UNSUPPORTED
+    assert st([0, 200, 512])[0] == _lib.QL_ERR_UNSUPPORTED          # not a multiple of 128
+    assert st([0, 128, 256, 384, 448, 512])[0] == _lib.QL_ERR_UNSUPPORTED  # 5 branches
+    assert st([0, 256, 256, 512])[0] == _lib.QL_ERR_ARG             # empty branch
+    assert st([0, 256, 500])[0] == _lib.QL_ERR_ARG                  # does not end at K
+    assert st([128, 256, 512])[0] == _lib.QL_ERR_ARG                # does not start at 0
+    d = _desc(K=512, n_k_segments=2, k_seg_offsets=None)
+    assert _plan_status(d)[0] == _lib.QL_ERR_ARG
+    assert _plan_status(_desc(n_k_segments=-1))[0] == _lib.QL_ERR_ARG

@@ -7,7 +7,8 @@ import numpy as np
 import pytest
 
 import oracle
-from tests.parity import (assert_close, assert_codes, compare_codes, say, unpack_codes)
+from tests.parity import (assert_close, assert_codes, compare_codes, compare_codes_scaled, say,
+                          unpack_codes)
 from workloads import configs, synth
 
 pytestmark = pytest.mark.gpu
@@ -172,6 +173,72 @@ def check_single(torch, X, W, *, M, K, N, B, w_bits=8, a_bits=8, cfg=0, guidance
     return dict(y_exact=exact, acc_max=int(np.abs(acc_o).max()))
 
 
+def check_kseg(torch, X, W, *, M, K, N, offs, w_bits=8, a_bits=8, B=0, a_scale="dual",
+               x_dtype="f32", cfg=0, guidance=4.0, lsb_k=0, static_scales=None, w_lsb_k=0,
+               rows=None, tag=""):
+    """SegLinear input branches on the GPU against the oracle: per-branch
+    weight codes and scales, per-branch activation scales and codes, every
+    branch's accumulators, and Y."""
+    from bit_post_quantization_amd import QuantLinear
+    S = len(offs) - 1
+    say(f"[kseg] {tag} M={M} K={K} N={N} offs={offs} w{w_bits}a{a_bits} B={B} {a_scale} "
+        f"{x_dtype} cfg={cfg} k={lsb_k} wk={w_lsb_k} static={static_scales is not None}")
+    ql = QuantLinear(_dev(torch, W), w_bits=w_bits, a_bits=a_bits, hadamard_block=B,
+                     a_scale=a_scale, x_dtype=x_dtype, k_seg_offsets=offs)
+    wp = oracle.InputSegmentedPlan(W, w_bits, offs, B=B)
+    check_weights(torch, ql, wp)
+    if w_lsb_k:
+        view = ql.lsb_view(w_lsb_k)
+        ql.plan.destroy()
+        ql, wp = view, wp.truncated(w_lsb_k)
+        check_weights(torch, ql, wp)
+    Xd = _dev(torch, X) if x_dtype == "f32" else _dev(torch, X.view(np.int16))
+    ss = None if static_scales is None else _dev(torch, np.asarray(static_scales, np.float32).reshape(-1))
+    codes_d, s_d = ql.quantize(Xd, lsb_k=lsb_k, static_scales=ss)
+    torch.cuda.synchronize()
+    codes_g = unpack_codes(codes_d.cpu().numpy(), K, a_bits)
+    s_g = s_d.cpu().numpy().reshape(S, 2)
+    codes_o, s_o = oracle.quantize_activations_segmented(
+        X, a_bits, offs, B=B, mode=a_scale, lsb_k=lsb_k, static_scales=static_scales,
+        bf16=x_dtype == "bf16")
+    assert np.array_equal(s_g.view(np.uint32), s_o.view(np.uint32)), f"act scales {s_g} vs {s_o}"
+    x32 = oracle.bf16_to_f32(X) if x_dtype == "bf16" else X
+    x_rot = np.concatenate([oracle.rotate(x32[:, a:b], B) if B else x32[:, a:b]
+                            for a, b in zip(offs[:-1], offs[1:])], axis=1)
+    s_el = np.concatenate([np.tile(s_o[j], (M, (b - a), 1)) for j, (a, b) in
+                           enumerate(zip(offs[:-1], offs[1:]))], axis=1)
+    st = compare_codes_scaled(codes_g, codes_o, x_rot, s_el)
+    assert_codes(st)
+    Mo = M // 2 if cfg else M
+    Yd = torch.empty((Mo, N), dtype=torch.float32, device="cuda")
+    dbg = torch.empty((2 * S, M, N), dtype=torch.int32, device="cuda")
+    ql.gemm(codes_d, s_d, cfg=cfg, w=guidance, Y=Yd, acc_dbg=dbg)
+    Yd2 = torch.empty_like(Yd)
+    ql.gemm(codes_d, s_d, cfg=cfg, w=guidance, Y=Yd2)
+    torch.cuda.synchronize()
+    assert torch.equal(Yd.view(torch.int32), Yd2.view(torch.int32)), "Y differs without acc dump"
+    out_rows = np.arange(Mo) if rows is None else np.asarray(rows)
+    acc_rows = np.concatenate([out_rows, out_rows + M // 2]) if cfg else out_rows
+    idx = torch.from_numpy(acc_rows).cuda()
+    y_o, accs = oracle.linear_segmented_rows(codes_g, s_g, wp, acc_rows, a_scale)
+    for j, (ap_o, an_o) in enumerate(accs):
+        ap_g = dbg[2 * j].index_select(0, idx).cpu().numpy()
+        an_g = dbg[2 * j + 1].index_select(0, idx).cpu().numpy()
+        if a_scale == "symmetric":
+            assert np.array_equal(ap_g.astype(np.int64), ap_o.astype(np.int64) + an_o), f"acc {j}"
+        else:
+            assert np.array_equal(ap_g, ap_o) and np.array_equal(an_g, an_o), f"acc {j}"
+    if cfg:
+        h = out_rows.size
+        ref = oracle.cfg_combine(y_o[:h], y_o[h:], guidance)
+    else:
+        ref = y_o
+    Y_g = Yd.index_select(0, torch.from_numpy(out_rows).cuda()).cpu().numpy()
+    e = assert_close(Y_g, ref, "Y")
+    say(f"  codes {st}; acc exact; Y max rel err {e:.3g}; "
+        f"bit-exact={np.array_equal(Y_g.view(np.uint32), ref.view(np.uint32))}")
+
+
 # ---------------------------------------------------------------- small ----
 
 def test_config1_full(torch):
@@ -275,6 +342,37 @@ def test_single_hadamard_rejects_dual_scales(torch):
         QuantLinear(W, hadamard_block=128, a_scale="dual", single_hadamard=True)
     with pytest.raises(QLError):
         QuantLinear(W, hadamard_block=0, a_scale="symmetric", single_hadamard=True)
+
+
+@pytest.mark.parametrize("M,K,N,offs,w_bits,a_bits,B,a_scale,cfg,x_dtype", [
+    (130, 512, 96, [0, 256, 512], 8, 8, 0, "dual", 1, "f32"),
+    (200, 384, 100, [0, 128, 384], 8, 4, 0, "dual", 0, "f32"),
+    (98, 1152, 80, [0, 768, 1152], 4, 4, 128, "dual", 1, "f32"),
+    (64, 640, 144, [0, 128, 256, 512, 640], 8, 8, 0, "symmetric", 0, "bf16"),
+    (66, 2304, 72, [0, 1152, 2304], 8, 8, 128, "symmetric", 1, "f32"),
+    (2, 272, 1, [0, 256, 272], 8, 8, 0, "dual", 1, "f32")])
+def test_input_branches(torch, M, K, N, offs, w_bits, a_bits, B, a_scale, cfg, x_dtype):
+    # Branches with different distributions: GELU with outliers, then a
+    # narrower SiLU, then N(0,1) scaled down (each branch on its own range).
+    parts, kinds = [], [synth.gelu_with_outliers, synth.silu_normal, synth.gelu_normal]
+    for j, (a, b) in enumerate(zip(offs[:-1], offs[1:])):
+        xj = kinds[j % 3](41, f"kseg/{M}{K}{N}/{j}", M, b - a) * np.float32(4.0 ** -j)
+        parts.append(xj.astype(np.float32))
+    X = np.concatenate(parts, axis=1)
+    if x_dtype == "bf16":
+        X = synth.f32_to_bf16_bits(X)
+    W = synth.weight_normal(41, f"kseg/W{M}{K}{N}", N, K)
+    check_kseg(torch, X, W, M=M, K=K, N=N, offs=offs, w_bits=w_bits, a_bits=a_bits, B=B,
+               a_scale=a_scale, x_dtype=x_dtype, cfg=cfg, tag="kseg")
+
+
+def test_input_branches_static_lsb_view(torch):
+    M, K, N, offs = 96, 768, 64, [0, 512, 768]
+    X = np.concatenate([synth.silu_normal(42, "kseg/st/0", M, 512),
+                        synth.gelu_normal(42, "kseg/st/1", M, 256) * np.float32(0.01)], axis=1)
+    W = synth.weight_normal(42, "kseg/st/W", N, K)
+    check_kseg(torch, X, W, M=M, K=K, N=N, offs=offs, cfg=1, lsb_k=2, w_lsb_k=3,
+               static_scales=[[0.02, 0.003], [0.0002, 0.0001]], tag="static+lsb+view")
 
 
 def test_weight_lsb_update(torch):
