@@ -37,7 +37,7 @@ def parse():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=50)
     p.add_argument("--warmup", type=int, default=10)
-    p.add_argument("--workload", default="mlp", help="mlp (default) | block | c3 | c3s | c4 | c4g | c5 | c6")
+    p.add_argument("--workload", default="mlp", help="mlp (default) | block | c3 | c3s | c4 | c4g | c5 | c6 | c7 | c7f")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=12.0,
                    help="approximate CPU time budget of the oracle baseline")
@@ -58,6 +58,9 @@ def layers_for(name):
     if name in ("c3", "c4"):
         wl = configs.WORKLOADS[name]
         return wl, list(wl.layers)
+    if name in ("c7", "c7f"):
+        wl = configs.WORKLOADS["c7"]
+        return wl, list(wl.layers)
     if name == "c3s":
         return configs.WORKLOADS["c3"], list(configs.c3_single())
     if name == "c4g":
@@ -72,7 +75,7 @@ def layers_for(name):
 
 
 class Layer:
-    def __init__(self, torch, wl, L):
+    def __init__(self, torch, wl, L, use_branches=True):
         from bit_post_quantization_amd import QuantLinear
         from workloads import configs
         self.L, self.M = L, wl.M
@@ -85,10 +88,12 @@ class Layer:
         self.ql = QuantLinear(Wd, w_bits=L.w_bits, a_bits=L.a_bits, hadamard_block=L.hadamard_block,
                               seg_offsets=None if seg is None else seg.tolist(),
                               w_scale=L.w_scale, a_scale=L.a_scale, x_dtype=L.x_dtype,
-                              single_hadamard=L.single_hadamard)
+                              single_hadamard=L.single_hadamard,
+                              k_seg_offsets=list(L.k_seg) if (L.k_seg and use_branches) else None)
         del Wd
         self.codes = self.ql.alloc_codes(self.M)
-        self.scales = torch.empty(2, dtype=torch.float32, device="cuda")
+        nks = max(1, len(L.k_seg) - 1) if use_branches else 1
+        self.scales = torch.empty(2 * nks, dtype=torch.float32, device="cuda")
         rows = self.M // 2 if L.cfg else self.M
         self.Y = torch.empty((rows, L.N), dtype=torch.float32, device="cuda")
         # algorithmic work
@@ -115,11 +120,14 @@ DATA = {
                      "N(0,0.02) weights)",
     "bf16_normal": "synthetic (seeded bf16(N(0,1)) activations, N(0,0.02) weights)",
     "silu": "synthetic (seeded SiLU(N(0,1)) activations, N(0,0.02) weights)",
+    "branches": "synthetic (seeded concatenated branches: GELU(N(0,1)) with outliers, "
+                "SiLU(N(0,1)), sin(3 N(0,1)); N(0,0.02) weights)",
 }
 SHAPE = {
     "c2": {"images": 16, "tokens_per_image": 256},
     "c3": {"images": 16, "tokens_per_image": 256},
     "c4": {"images": 4, "tokens_per_image": 4608},
+    "c7": {"images": 16, "tokens_per_image": 256},
 }
 
 
@@ -411,7 +419,7 @@ def main():
         bench_tasq_weight_sweep(torch, args)
         return
     wl, Ls = layers_for(args.workload)
-    layers = [Layer(torch, wl, L) for L in Ls]
+    layers = [Layer(torch, wl, L, use_branches=args.workload != "c7f") for L in Ls]
     torch.cuda.synchronize()
 
     ev = lambda: torch.cuda.Event(enable_timing=True)  # noqa: E731
@@ -505,7 +513,11 @@ def main():
                          "c3s": "DiT-XL/2 block W4A4, single Hadamard-128 on X only "
                                 "(W as H W_int^T), symmetric activations",
                          "c4": "MM-DiT SegLinear layers W4 A4/A8",
-                         "c4g": "MM-DiT SegLinear layers W4, A4/A8 by the greedy allocation"
+                         "c4g": "MM-DiT SegLinear layers W4, A4/A8 by the greedy allocation",
+                         "c7": "SegLinear input branches: [hidden|skip] 2304->1152 and "
+                               "[temb 256|hidden 1152] 1408->1152, W8A8, CFG",
+                         "c7f": "the c7 layers and inputs with one scale pair per tensor "
+                                "(no input branches), for comparison"
                          }[args.workload],
             "M": wl.M, **SHAPE[wl.key], "cfg_guidance": first.guidance if first.cfg else None,
             "w_bits": first.w_bits, "a_bits": per_layer_or_one([L.a_bits for L in Ls]),

@@ -499,13 +499,21 @@ __device__ __forceinline__ void gemm_wave(const GemmArgs& g, int wave, int lane,
   // back (from L2) by the next branch end or by the tile epilogue. Also the
   // current branch and the K-step at which it ends.
   static_assert(!KS || 2 * NBW * 4 <= kYSlots, "partial-sum slots");
-  float* const yws = KS ? g.ypart_ws + (int64_t)blockIdx.x * kYSlots * kThreads + threadIdx.x
-                        : nullptr;
-  auto yslot = [&](int fi, int jj, int r) __attribute__((always_inline)) {
-    return yws + ((fi * NBW + jj) * 4 + r) * kThreads;
+  // Buffer accesses: the workgroup's block in the descriptor, the thread in
+  // one vector offset, the slot in the scalar offset (no per-slot addresses).
+  const __amdgpu_buffer_rsrc_t ryw =
+      make_rsrc(KS ? g.ypart_ws + (int64_t)blockIdx.x * kYSlots * kThreads : g.Y,
+                KS ? (uint32_t)(kYSlots * kThreads * 4) : 0u);
+  const unsigned ytid = 4u * threadIdx.x;
+  auto yoff = [&](int fi, int jj, int r) __attribute__((always_inline)) {
+    return (unsigned)(((fi * NBW + jj) * 4 + r) * kThreads * 4);
   };
+  // Loads bypass the L1 (glc): the slot was last written by this thread.
   auto yload = [&](int fi, int jj, int r) __attribute__((always_inline)) {
-    return __hip_atomic_load(yslot(fi, jj, r), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    return __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(ryw, ytid, yoff(fi, jj, r), 1));
+  };
+  auto ystore = [&](int fi, int jj, int r, float v) __attribute__((always_inline)) {
+    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), ryw, ytid, yoff(fi, jj, r), 0);
   };
   int cur_seg = 0;
   int seg_end = KS ? g.ks_end[0] : 0;
@@ -547,9 +555,10 @@ __device__ __forceinline__ void gemm_wave(const GemmArgs& g, int wave, int lane,
       }
   };
 
-  // End of input branch cur_seg inside a tile: add its epilogue part to
-  // ypart (fp32, branch order) and let the accumulators restart. The scale
-  // loads and any dump stores drain before the K loop goes on.
+  // End of input branch cur_seg of a tile: add its epilogue part (before
+  // 1/B) to the partial sums (fp32, branch order) in the workspace; the
+  // caller restarts the accumulators. The scale loads and the stores drain
+  // before the K loop goes on, so the next reload finds the sums in L2.
   auto fold = [&](int ti) __attribute__((always_inline)) {
     int m0, n0;
     coords(ti, m0, n0);
@@ -583,7 +592,7 @@ __device__ __forceinline__ void gemm_wave(const GemmArgs& g, int wave, int lane,
           accs(fi, jj, r, ap, an);
           float y = epi_part<SYM>(ap, an, spj, snj, swj[jj]);
           if (j > 0) y = __fadd_rn(old[fi][jj], y);
-          if constexpr (KS) *yslot(fi, jj, r) = y;
+          if constexpr (KS) ystore(fi, jj, r, y);
         }
       asm volatile("" ::: "memory");
     }
@@ -681,29 +690,10 @@ __device__ __forceinline__ void gemm_wave(const GemmArgs& g, int wave, int lane,
     }
 #pragma unroll
     for (int jj = 0; jj < NBW; ++jj) asm volatile("" ::"v"(sw[jj]));
-    // With input branches, the finished branches' sums of accumulator row r
-    // (reloaded one row at a time).
-    float yp[KS ? 2 : 1][KS ? NBW : 1];
-    auto load_yp = [&](int r) __attribute__((always_inline)) {
-      if constexpr (KS) {
-        asm volatile("" ::: "memory");
-#pragma unroll
-        for (int fi = 0; fi < 2; ++fi)
-#pragma unroll
-          for (int jj = 0; jj < NBW; ++jj) yp[fi][jj] = yload(fi, jj, r);
-      }
-    };
-    // Output of slot (fi, jj, r): with input branches, the finished
-    // branches' sum plus this branch's part, then the rotation's 1/B.
     auto yout = [&](int fi, int jj, int r) __attribute__((always_inline)) {
       int ap, an;
       accs(fi, jj, r, ap, an);
-      if constexpr (KS) {
-        const float y = __fadd_rn(yp[fi][jj], epi_part<SYM>(ap, an, sp, sn, sw[jj]));
-        return __fmul_rn(y, g.inv_b);
-      } else {
-        return epi<SYM>(ap, an, sp, sn, sw[jj], g.inv_b);
-      }
+      return epi<SYM>(ap, an, sp, sn, sw[jj], g.inv_b);
     };
     const int rows_here = min(RPT, (CFG ? g.Mh : g.M) - m0);
     const __amdgpu_buffer_rsrc_t ry =
@@ -711,7 +701,6 @@ __device__ __forceinline__ void gemm_wave(const GemmArgs& g, int wave, int lane,
     const unsigned rowb = (unsigned)g.N * 4u;
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      load_yp(r);
       if constexpr (CFG) {
         const unsigned ro = (unsigned)(16 * band + rsub + r) * rowb;
 #pragma unroll
@@ -738,6 +727,55 @@ __device__ __forceinline__ void gemm_wave(const GemmArgs& g, int wave, int lane,
     // Let the stores complete here, while no load is in flight: pending
     // stores would otherwise leave the compiler unable to account the loads
     // of the next steps, and it would drain the whole load stream later.
+    wait_vmcnt<0>();
+  };
+
+  // Tile epilogue with input branches: the last branch is folded like the
+  // others (its sum now complete in the workspace), then the sums are read
+  // back a row at a time, scaled by 1/B, combined for CFG and stored; the
+  // accumulators are no longer live by then.
+  auto epilogue_ks = [&](int ti) __attribute__((always_inline)) {
+    fold(ti);
+    int m0, n0;
+    coords(ti, m0, n0);
+    unsigned coff[NBW];
+#pragma unroll
+    for (int jj = 0; jj < NBW; ++jj) {
+      const int col = n0 + 16 * (J0 + jj) + i16;
+      coff[jj] = col < g.N ? 4u * (unsigned)col : kOOB;
+    }
+    const int rows_here = min(RPT, (CFG ? g.Mh : g.M) - m0);
+    const __amdgpu_buffer_rsrc_t ry =
+        make_rsrc(g.Y + (int64_t)m0 * g.N, (uint32_t)rows_here * (uint32_t)g.N * 4u);
+    const unsigned rowb = (unsigned)g.N * 4u;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      float y[2][NBW];
+#pragma unroll
+      for (int fi = 0; fi < 2; ++fi)
+#pragma unroll
+        for (int jj = 0; jj < NBW; ++jj) y[fi][jj] = __fmul_rn(yload(fi, jj, r), g.inv_b);
+      if constexpr (CFG) {
+        const unsigned ro = (unsigned)(16 * band + rsub + r) * rowb;
+#pragma unroll
+        for (int jj = 0; jj < NBW; ++jj) {
+          const float d = __fsub_rn(y[0][jj], y[1][jj]);
+          const float t = __fmul_rn(g.guidance, d);
+          __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(__fadd_rn(y[1][jj], t)), ry,
+                                                ro + coff[jj], 0, 0);
+        }
+      } else {
+#pragma unroll
+        for (int fi = 0; fi < 2; ++fi) {
+          const unsigned ro = (unsigned)(16 * (2 * band + fi) + rsub + r) * rowb;
+#pragma unroll
+          for (int jj = 0; jj < NBW; ++jj)
+            __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(y[fi][jj]), ry,
+                                                  ro + coff[jj], 0, 0);
+        }
+      }
+      asm volatile("" ::: "memory");
+    }
     wait_vmcnt<0>();
   };
 
@@ -777,6 +815,8 @@ __device__ __forceinline__ void gemm_wave(const GemmArgs& g, int wave, int lane,
     if (step(s, uc)) {
       if constexpr (HS)
         epilogue_hs(cmp_ti);
+      else if constexpr (KS)
+        epilogue_ks(cmp_ti);
       else
         epilogue(cmp_ti);
       zero_acc();

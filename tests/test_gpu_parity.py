@@ -592,6 +592,18 @@ def test_config3_single_hadamard(torch, li):
                  tag=f"c3s/{L.name}")
 
 
+@pytest.mark.timeout(600)
+@pytest.mark.parametrize("li", range(2))
+def test_config7_input_branches(torch, li):
+    wl = configs.WORKLOADS["c7"]
+    L = wl.layers[li]
+    X = configs.make_x(wl, L)
+    W = configs.make_w(wl, L)
+    rows = sample_rows(wl.M, True, 48, seed=300 + li)
+    check_kseg(torch, X, W, M=wl.M, K=L.K, N=L.N, offs=list(L.k_seg), cfg=1,
+               guidance=L.guidance, rows=rows, tag=f"c7/{L.name}")
+
+
 @pytest.mark.timeout(900)
 @pytest.mark.parametrize("li", range(4))
 def test_config4_mmdit_segments(torch, li):

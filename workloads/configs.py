@@ -36,6 +36,8 @@ class Layer:
     cfg: bool = False
     guidance: float = 4.0
     single_hadamard: bool = False     # rotate X only (W enters as H W_int^T)
+    k_seg: Tuple[int, ...] = ()       # input branch offsets (SegLinear input segmentation)
+    branch_kinds: Tuple[str, ...] = ()  # x_kind of each input branch
 
     def seg_offsets(self) -> Optional[np.ndarray]:
         if self.n_segments <= 1:
@@ -126,7 +128,19 @@ def _c6() -> Workload:
         steps=50, lsb_choices=(0, 2, 4), stages=4)
 
 
-WORKLOADS = {w.key: w for w in (_c1(), _c2(), _c3(), _c4(), _c5(), _c6())}
+def _c7() -> Workload:
+    return Workload(
+        key="c7", title="SegLinear input branches at DiT-XL/2 width, W8A8 DualScale, CFG-paired "
+                        "M=4096: a skip fusion [hidden 1152 | skip 1152] -> 1152 and a "
+                        "conditioning fusion [timestep embedding 256 | hidden 1152] -> 1152",
+        M=4096,
+        layers=(Layer("skip", 2304, 1152, x_kind="branches", cfg=True, k_seg=(0, 1152, 2304),
+                      branch_kinds=("gelu_outliers", "silu")),
+                Layer("temb", 1408, 1152, x_kind="branches", cfg=True, k_seg=(0, 256, 1408),
+                      branch_kinds=("sinusoid", "gelu_outliers"))))
+
+
+WORKLOADS = {w.key: w for w in (_c1(), _c2(), _c3(), _c4(), _c5(), _c6(), _c7())}
 
 
 def c6_w_schedule(seed: int = SEED) -> np.ndarray:
@@ -175,6 +189,12 @@ def make_x(wl: Workload, layer: Layer, M: Optional[int] = None, step: Optional[i
         return synth.gelu_with_outliers(seed, name, M, layer.K)
     if layer.x_kind == "bf16_normal":
         return synth.bf16_normal(seed, name, M, layer.K)
+    if layer.x_kind == "branches":
+        gen = {"silu": synth.silu_normal, "gelu_outliers": synth.gelu_with_outliers,
+               "sinusoid": synth.sinusoid}
+        return np.concatenate(
+            [gen[kd](seed, f"{name}/b{j}", M, b - a) for j, (kd, a, b) in
+             enumerate(zip(layer.branch_kinds, layer.k_seg[:-1], layer.k_seg[1:]))], axis=1)
     raise ValueError(layer.x_kind)
 
 

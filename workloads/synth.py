@@ -35,6 +35,13 @@ def gelu_normal(seed: int, name: str, M: int, K: int) -> np.ndarray:
     return (0.5 * z * (1.0 + erf(z / np.sqrt(2.0)))).astype(np.float32)
 
 
+def sinusoid(seed: int, name: str, M: int, K: int) -> np.ndarray:
+    """fp32 [M,K] = sin(3 z), z ~ N(0,1): bounded features in [-1, 1], like a
+    sinusoidal timestep embedding concatenated to a hidden state."""
+    z = normal_f64(seed, name, (M, K))
+    return np.sin(3.0 * z).astype(np.float32)
+
+
 def outlier_columns(seed: int, name: str, K: int, frac: float = 0.001) -> np.ndarray:
     """max(1, round(frac*K)) distinct channel indices, seeded, sorted."""
     cnt = max(1, int(round(frac * K)))
