@@ -403,7 +403,7 @@ def bench_tasq_weight_sweep(torch, args):
 def main():
     args = parse()
     if args.gpus != 1:
-        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1"}))
+        print(json.dumps({"error": "the quantized linear runs on one GPU; --gpus must be 1"}))
         raise SystemExit(2)
     import torch
     assert torch.cuda.is_available(), "bench needs a GPU"
