@@ -27,7 +27,11 @@
  *     the library never frees or retains them. Host pointers are marked HOST.
  *   - `stream` is a hipStream_t passed as void* (NULL = the null stream).
  *     All work is enqueued asynchronously on it; no call synchronises the
- *     host or copies device data to the host, except qlinear_plan (below).
+ *     host or copies device data to the host, except qlinear_plan and
+ *     qlinear_plan_lsb_view (below). qlinear_quantize_act, qlinear_gemm,
+ *     qlinear_cfg_combine and qlinear_plan_lsb_update enqueue kernel
+ *     launches only (no allocation, no memset), so they can be captured
+ *     into a HIP graph.
  *   - Arguments are validated on the host before anything is enqueued; a
  *     violation returns QL_ERR_ARG (or QL_ERR_UNSUPPORTED for a valid but
  *     unimplemented combination) and enqueues nothing. A failed HIP launch

@@ -524,6 +524,46 @@ def test_repeated_dynamic_calls_reset_workspace(torch):
         assert np.array_equal(s.cpu().numpy(), oracle.act_scales(X, 8)), i
 
 
+def test_graph_capture_replays(torch):
+    # quantize + gemm enqueue no allocation, memset or host synchronisation,
+    # so a step can be captured into a HIP graph: every replay (with new data
+    # in the captured input, eager work and synchronisation in between) must
+    # equal the eager result on the same data.
+    from bit_post_quantization_amd import QuantLinear
+    M, K, N = 256, 512, 192
+    ql = QuantLinear(_dev(torch, synth.weight_normal(27, "graph/W", N, K)))
+    X = torch.empty((M, K), dtype=torch.float32, device="cuda")
+    codes = ql.alloc_codes(M)
+    sc = torch.empty(2, dtype=torch.float32, device="cuda")
+    Y = torch.empty((M // 2, N), dtype=torch.float32, device="cuda")
+
+    def step():
+        ql.quantize(X, codes=codes, act_scales=sc)
+        ql.gemm(codes, sc, cfg=1, w=4.0, Y=Y)
+
+    X.copy_(_dev(torch, synth.silu_normal(27, "graph/X0", M, K)))
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        step()
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    for i in range(4):
+        X.copy_(_dev(torch, synth.gelu_with_outliers(27, f"graph/X{i + 1}", M, K)
+                     * np.float32(10.0 ** (i - 2))))
+        g.replay()
+        torch.cuda.synchronize()
+        y_graph = Y.clone()
+        s_graph = sc.clone()
+        step()  # eager on the same data
+        torch.cuda.synchronize()
+        assert torch.equal(s_graph.view(torch.int32), sc.view(torch.int32)), i
+        assert torch.equal(y_graph.view(torch.int32), Y.view(torch.int32)), i
+
+
 def test_cfg_combine_standalone(torch):
     from bit_post_quantization_amd import qlinear_cfg_combine
     for M, N in [(302, 77), (2, 1), (4096, 1152)]:
