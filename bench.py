@@ -224,6 +224,51 @@ def measured_traffic():
     return t.get("bytes_per_launch")
 
 
+def per_launch_rates(torch, calls):
+    """Run `calls` [(kind, fn, amount)] once with an event pair around every
+    launch (on the launching stream); per kind, the summed amount divided by
+    the summed durations, and the mean duration."""
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in calls]
+    torch.cuda.synchronize()
+    for (kind, fn, amount), (a, b) in zip(calls, ev):
+        a.record()
+        fn()
+        b.record()
+    torch.cuda.synchronize()
+    out = {}
+    for (kind, fn, amount), (a, b) in zip(calls, ev):
+        o = out.setdefault(kind, {"amount": 0.0, "s": 0.0, "n": 0})
+        o["amount"] += amount
+        o["s"] += a.elapsed_time(b) * 1e-3
+        o["n"] += 1
+    return {k: {"rate": v["amount"] / v["s"], "avg_us": v["s"] / v["n"] * 1e6}
+            for k, v in out.items()}
+
+
+def sweep_roofline(rates, ops_per_gemm, quant_bytes):
+    g, q = rates["gemm"], rates["quant"]
+    return ({"kernel": "k2_gemm (int8 MFMA, both polarity planes, fused epilogue)",
+             "bound": "mfma", "achieved": round(g["rate"] / 1e12, 1), "peak": PEAK_INT8_TOPS,
+             "unit": "TOPS", "frac": round(g["rate"] / 1e12 / PEAK_INT8_TOPS, 4),
+             "ops_per_launch": ops_per_gemm, "avg_launch_us": round(g["avg_us"], 2),
+             "traffic": None},
+            {"kernels": "k1 (quantize)", "bound": "hbm", "achieved": round(q["rate"] / 1e9, 1),
+             "peak": PEAK_HBM_GBPS, "unit": "GB/s",
+             "frac": round(q["rate"] / 1e9 / PEAK_HBM_GBPS, 4), "bytes_per_step": quant_bytes})
+
+
+class HostLayer:
+    """Host copies of one layer's synthetic inputs, for the oracle baseline."""
+
+    def __init__(self, wl, L):
+        from workloads import configs
+        self.L, self.M = L, wl.M
+        self.X_host = configs.make_x(wl, L, step=0)
+        self.W_host = configs.make_w(wl, L)
+        self.mfma_ops = 2 * 2.0 * wl.M * L.N * L.K
+
+
 def bench_tasq_sweep(torch, args):
     """The TASQ sweep: 28 DiT-XL/2 blocks x (qkv, proj, fc1, fc2) = 112 W8A8
     DualScale CFG linears per denoising step, each quantize call with the
@@ -274,6 +319,17 @@ def bench_tasq_sweep(torch, args):
     torch.cuda.synchronize()
     per = np.array([evs[t].elapsed_time(evs[t + 1]) for t in range(steps)])
     total_ms = float(per.sum())
+    calls = []
+    for li, (L, ql) in enumerate(zip(wl.layers, plans)):
+        X = pool[L.K][li % 4]
+        k = int(sched[0, li])
+        calls.append(("quant", lambda ql=ql, X=X, L=L, k=k: qlinear_quantize_act(
+            ql.plan, X, M, k, None, codes[L.K], scales), M * L.K * 5.0))
+        calls.append(("gemm", lambda ql=ql, L=L: qlinear_gemm(
+            ql.plan, codes[L.K], scales, M, 1, L.guidance, ys[L.N]), 4.0 * M * L.N * L.K))
+    roof, quant = sweep_roofline(per_launch_rates(torch, calls),
+                                 ops_per_step / len(wl.layers),
+                                 sum(M * L.K * 5.0 for L in wl.layers))
     out = {
         "metric": "quantized-linear int8 TOPS (% MFMA peak), TASQ 50-step sweep",
         "value": round(ops_per_step * steps / (total_ms * 1e-3) / 1e12, 2), "unit": "TOPS",
@@ -288,8 +344,20 @@ def bench_tasq_sweep(torch, args):
                           "median": round(ops_per_step / (np.median(per) * 1e-3) / 1e12, 1),
                           "max": round(ops_per_step / (per.min() * 1e-3) / 1e12, 1)},
         "mfma_ops_per_step": ops_per_step,
+        "roofline": roof, "act_quant": quant,
     }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = sweep_cpu_baseline(wl, args.cpu_seconds)
     print(json.dumps(out), flush=True)
+
+
+def sweep_cpu_baseline(wl, budget_s):
+    """The oracle on one block of the sweep (its four linears at step 0,
+    host-generated inputs of the same recipe), as TOPS; a rate, so it holds
+    for the whole sweep."""
+    cb = cpu_baseline([HostLayer(wl, L) for L in wl.layers[:4]], budget_s)
+    cb["sample"] = "one block (qkv, proj, fc1, fc2) at step 0: " + cb["sample"]
+    return cb
 
 
 def bench_tasq_weight_sweep(torch, args):
@@ -377,6 +445,16 @@ def bench_tasq_weight_sweep(torch, args):
     per = np.array([evs[t].elapsed_time(evs[t + 1]) for t in range(steps)])
     total_ms = float(per.sum())
     wbytes = sum(L.N * L.K for L in wl.layers)
+    calls = []
+    for li, (L, v) in enumerate(zip(wl.layers, views)):
+        X = pool[L.K][li % 4]
+        calls.append(("quant", lambda v=v, X=X, L=L, li=li: qlinear_quantize_act(
+            v.plan, X, M, 0, table[0, li], codes[L.K], scales), M * L.K * 5.0))
+        calls.append(("gemm", lambda v=v, L=L: qlinear_gemm(
+            v.plan, codes[L.K], scales, M, 1, L.guidance, ys[L.N]), 4.0 * M * L.N * L.K))
+    roof, quant = sweep_roofline(per_launch_rates(torch, calls),
+                                 ops_per_step / len(wl.layers),
+                                 sum(M * L.K * 5.0 for L in wl.layers))
     out = {
         "metric": "quantized-linear int8 TOPS (% MFMA peak), TASQ weight-side 50-step sweep",
         "value": round(ops_per_step * steps / (total_ms * 1e-3) / 1e12, 2), "unit": "TOPS",
@@ -396,7 +474,10 @@ def bench_tasq_weight_sweep(torch, args):
         "rewrite_all_views_GBps": round(2.0 * wbytes / (rewrite_all_ms * 1e-3) / 1e9, 1),
         "weight_bytes_stored_plus_views": 2 * wbytes,
         "mfma_ops_per_step": ops_per_step,
+        "roofline": roof, "act_quant": quant,
     }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = sweep_cpu_baseline(wl, args.cpu_seconds)
     print(json.dumps(out), flush=True)
 
 
