@@ -5,6 +5,7 @@ import ctypes
 import os
 import re
 import subprocess
+import sys
 
 import pytest
 
@@ -137,3 +138,11 @@ def test_plan_rejects_bad_input_branches():
     d = _desc(K=512, n_k_segments=2, k_seg_offsets=None)
     assert _plan_status(d)[0] == _lib.QL_ERR_ARG
     assert _plan_status(_desc(n_k_segments=-1))[0] == _lib.QL_ERR_ARG
+
+
+def test_bench_refuses_more_than_one_gpu():
+    import json as _json
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True, timeout=120)
+    assert r.returncode == 2
+    assert "one GPU" in _json.loads(r.stdout.strip().splitlines()[-1])["error"]
