@@ -206,9 +206,16 @@ def copy_calibration(torch):
 
 
 def gemm_source_hash():
+    """SHA-256 of the GEMM source's code: comments and blank lines removed,
+    so that editing a comment does not invalidate a profile."""
     import hashlib
-    with open(GEMM_SOURCE, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()
+    import re
+    with open(GEMM_SOURCE) as f:
+        src = f.read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    src = re.sub(r"//[^\n]*", "", src)
+    code = "\n".join(line.rstrip() for line in src.splitlines() if line.strip())
+    return hashlib.sha256(code.encode()).hexdigest()
 
 
 def measured_traffic():

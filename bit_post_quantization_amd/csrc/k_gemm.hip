@@ -41,6 +41,14 @@
 //  * CFG pairing: a row band is 16 conditional rows and their 16
 //    unconditional partners (fragments 0 and 1), so a lane holds both
 //    accumulators of a pair in the same register slot.
+//  * Single Hadamard (HQ-DM explainer 2.1, activations rotated only): the
+//    plan's weight rows hold hi and lo int8 planes of H W_int^T in adjacent
+//    16-row fragments; the symmetric kernel multiplies both and the epilogue
+//    combines each pair exactly in fp64 (epilogue_hs).
+//  * Input branches (SegQuant explainer 2.A, input segmentation): when the
+//    K loop crosses a branch end, the branch's epilogue part is folded into
+//    fp32 partial sums held in a per-thread workspace slice and the
+//    accumulators restart (fold, epilogue_ks).
 #include <type_traits>
 
 #include "ql_device.h"

@@ -22,7 +22,7 @@ struct qlinear_plan {
                              // H W_int^T, int8 [2 * roundup(N,16), K] (single Hadamard)
   uint8_t* wint = nullptr;   // single Hadamard: the codes W_int, int8 [N,K]
   float* ypart = nullptr;    // input branches: the GEMM's partial-sum workspace
-  float* sw = nullptr;       // weight scales [N]
+  float* sw = nullptr;       // weight scales [nks, N]
   ql::ReduceWs* ws = nullptr;
 };
 
@@ -240,14 +240,16 @@ ql_status qlinear_plan(const ql_desc* d, const float* W, void* stream, qlinear_p
     if (rowmax) (void)hipFree(rowmax);
     if (segd) (void)hipFree(segd);
   };
-#define QL_TRY(expr, what)          \
-  do {                              \
-    e = (expr);                     \
-    if (e != hipSuccess) {          \
-      cleanup();                    \
-      free_plan(p);                 \
-      return hip_fail(e, what);     \
-    }                               \
+  // On failure, let the work already enqueued finish before its buffers go.
+#define QL_TRY(expr, what)                \
+  do {                                    \
+    e = (expr);                           \
+    if (e != hipSuccess) {                \
+      (void)hipStreamSynchronize(s);      \
+      cleanup();                          \
+      free_plan(p);                       \
+      return hip_fail(e, what);           \
+    }                                     \
   } while (0)
   QL_TRY(hipMalloc(&p->wq, gbytes), "allocating weight codes");
   if (single) QL_TRY(hipMalloc(&p->wint, wbytes), "allocating unrotated weight codes");
