@@ -18,11 +18,16 @@
  *          technical summary section 2: A SegLinear, B DualScale.
  *   [CFG] "Closing the Null Space: Guidance-Aware Quantization for
  *          Classifier-Free Diffusion", problem statement (guided prediction)
- *          and methodology (dual-branch calibration).
+ *          and methodology (dual-branch calibration, greedy allocation of
+ *          activation bits).
  *   [HQ]  "HQ-DM: Single Hadamard Transformation-Based Quantization-Aware
- *          Training for Low-Bit Diffusion Models", technical summary 2.1.
+ *          Training for Low-Bit Diffusion Models", technical summary 2.1
+ *          (block rotation, single transform) and 2.2 (symmetric scales).
  *   [TQ]  "TASQ: Temporal-Adaptive Bit Sparsification Quantization for
- *          Diffusion Models", technical summary section 2 (LSB mask).
+ *          Diffusion Models", technical summary section 2 (LSB mask, on the
+ *          activation codes and on the shared weight codes).
+ * Input segmentation ([SQ] 2.A) and the pipeline helpers are composed in
+ * oracle/__init__.py from the functions below.
  *
  * Parity pins: every function is pinned by tests against closed forms,
  * invariants, library routines or brute force (see the oracle tests).
