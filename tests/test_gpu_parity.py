@@ -175,7 +175,7 @@ def check_single(torch, X, W, *, M, K, N, B, w_bits=8, a_bits=8, cfg=0, guidance
 
 def check_kseg(torch, X, W, *, M, K, N, offs, w_bits=8, a_bits=8, B=0, a_scale="dual",
                x_dtype="f32", cfg=0, guidance=4.0, lsb_k=0, static_scales=None, w_lsb_k=0,
-               rows=None, tag=""):
+               rows=None, w_scale="channel", seg=None, tag=""):
     """SegLinear input branches on the GPU against the oracle: per-branch
     weight codes and scales, per-branch activation scales and codes, every
     branch's accumulators, and Y."""
@@ -184,8 +184,9 @@ def check_kseg(torch, X, W, *, M, K, N, offs, w_bits=8, a_bits=8, B=0, a_scale="
     say(f"[kseg] {tag} M={M} K={K} N={N} offs={offs} w{w_bits}a{a_bits} B={B} {a_scale} "
         f"{x_dtype} cfg={cfg} k={lsb_k} wk={w_lsb_k} static={static_scales is not None}")
     ql = QuantLinear(_dev(torch, W), w_bits=w_bits, a_bits=a_bits, hadamard_block=B,
-                     a_scale=a_scale, x_dtype=x_dtype, k_seg_offsets=offs)
-    wp = oracle.InputSegmentedPlan(W, w_bits, offs, B=B)
+                     a_scale=a_scale, x_dtype=x_dtype, k_seg_offsets=offs, w_scale=w_scale,
+                     seg_offsets=seg)
+    wp = oracle.InputSegmentedPlan(W, w_bits, offs, B=B, mode=w_scale, seg_offsets=seg)
     check_weights(torch, ql, wp)
     if w_lsb_k:
         view = ql.lsb_view(w_lsb_k)
@@ -364,6 +365,20 @@ def test_input_branches(torch, M, K, N, offs, w_bits, a_bits, B, a_scale, cfg, x
     W = synth.weight_normal(41, f"kseg/W{M}{K}{N}", N, K)
     check_kseg(torch, X, W, M=M, K=K, N=N, offs=offs, w_bits=w_bits, a_bits=a_bits, B=B,
                a_scale=a_scale, x_dtype=x_dtype, cfg=cfg, tag="kseg")
+
+
+@pytest.mark.parametrize("w_scale,seg,a_bits,x_dtype", [
+    ("segment", [0, 48, 96, 144], 8, "f32"), ("tensor", None, 4, "bf16")])
+def test_input_branches_with_output_segments(torch, w_scale, seg, a_bits, x_dtype):
+    # Input branches and output-segment (or per-tensor) weight scales together.
+    M, K, N, offs = 100, 640, 144, [0, 384, 640]
+    X = np.concatenate([synth.silu_normal(43, "kseg/os/0", M, 384),
+                        synth.sinusoid(43, "kseg/os/1", M, 256)], axis=1)
+    if x_dtype == "bf16":
+        X = synth.f32_to_bf16_bits(X)
+    W = synth.weight_normal(43, "kseg/os/W", N, K)
+    check_kseg(torch, X, W, M=M, K=K, N=N, offs=offs, w_bits=4, a_bits=a_bits, cfg=1,
+               x_dtype=x_dtype, w_scale=w_scale, seg=seg, tag=f"kseg+{w_scale}")
 
 
 def test_input_branches_static_lsb_view(torch):
