@@ -515,6 +515,25 @@ def test_degenerate_inputs(torch):
     check_layer(torch, pos, Wz, M=M, K=K, N=N, tag="zero-weights")
 
 
+def test_extreme_magnitudes(torch):
+    # Subnormal inputs (subnormal scales: the reciprocal overflows and the
+    # exact division path takes over), a 1e-30 .. 1e30 dynamic range (most
+    # codes 0) and large values whose products stay finite.
+    M, K, N = 96, 256, 80
+    W = synth.weight_normal(28, "ext/W", N, K)
+    z = synth.normal_f64(28, "ext/z", (M, K))
+    sub = (z * 1e-40).astype(np.float32)
+    assert np.abs(sub).max() < np.finfo(np.float32).tiny
+    check_layer(torch, sub, W, M=M, K=K, N=N, cfg=1, tag="subnormal")
+    check_layer(torch, sub, W, M=M, K=K, N=N, a_bits=4, w_bits=4, B=64, a_scale="symmetric",
+                tag="subnormal-h64-a4")
+    wide = (np.sign(z) * 10.0 ** (60.0 * synth.normal_f64(28, "ext/e", (M, K)).clip(-1, 1) / 2)
+            ).astype(np.float32)
+    check_layer(torch, wide, W, M=M, K=K, N=N, cfg=1, tag="1e-30..1e30")
+    big = (z * 1e30).astype(np.float32)
+    check_layer(torch, big, W, M=M, K=K, N=N, B=128, tag="1e30")
+
+
 def test_empty_input_is_noop(torch):
     from bit_post_quantization_amd import QuantLinear
     W = _dev(torch, synth.weight_normal(7, "empty/W", 32, 64))
