@@ -146,3 +146,35 @@ def test_bench_refuses_more_than_one_gpu():
                        capture_output=True, text=True, timeout=120)
     assert r.returncode == 2
     assert "one GPU" in _json.loads(r.stdout.strip().splitlines()[-1])["error"]
+
+
+def test_header_compiles_and_links_as_c(tmp_path):
+    # A plain C99 client of include/qlinear.h, linked against libqlinear.so,
+    # exercising a host-side argument error (no GPU needed).
+    import shutil
+    gcc = shutil.which("gcc")
+    if gcc is None:
+        pytest.skip("gcc not found")
+    src = tmp_path / "client.c"
+    src.write_text(r"""
+#include <stdio.h>
+#include <string.h>
+#include "qlinear.h"
+int main(void) {
+  ql_desc d;
+  memset(&d, 0, sizeof d);
+  d.N = 64; d.K = 40; d.w_bits = 8; d.a_bits = 8; d.n_segments = 1;
+  qlinear_plan_t p = 0;
+  ql_status st = qlinear_plan(&d, (const float*)0x1000, NULL, &p);
+  printf("%d %s\n", (int)st, qlinear_last_error());
+  return st == QL_ERR_ARG && p == 0 ? 0 : 1;
+}
+""")
+    exe = tmp_path / "client"
+    libdir = os.path.dirname(_lib.LIB_PATH)
+    subprocess.run([gcc, "-std=c99", "-Wall", "-Werror", f"-I{os.path.join(ROOT, 'include')}",
+                    str(src), f"-L{libdir}", "-lqlinear", f"-Wl,-rpath,{libdir}", "-o", str(exe)],
+                   check=True, capture_output=True, text=True)
+    r = subprocess.run([str(exe)], capture_output=True, text=True, timeout=60)
+    assert r.returncode == 0, r.stdout + r.stderr
+    assert "multiple of 16" in r.stdout
