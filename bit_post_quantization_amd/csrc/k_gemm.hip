@@ -878,20 +878,34 @@ __global__ __launch_bounds__(kThreads, 1) void k2_gemm(GemmArgs g) {
     gemm_wave<A4, SYM, CFG, HS, KS, NB, 1, false>(g, wave, lane, st0, st1, st2, st3);
 }
 
-int g_cus = 0;  // compute units of the device (queried on first launch)
+// Compute units per device, queried on the first launch there. The grid
+// never exceeds the current device's count (a plan's partial-sum workspace
+// is sized by the same count).
+constexpr int kMaxDevices = 64;
+int g_cus[kMaxDevices] = {};
+
+hipError_t device_cus(int& cus) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  const bool cached = dev >= 0 && dev < kMaxDevices;
+  if (cached && g_cus[dev] > 0) {
+    cus = g_cus[dev];
+    return hipSuccess;
+  }
+  e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+  if (e == hipSuccess && cached) g_cus[dev] = cus;
+  return e;
+}
 
 template <bool A4, bool SYM, bool CFG, bool HS, bool KS, int NB>
 hipError_t run(const GemmArgs& g, hipStream_t s) {
   const int rpt = CFG ? 64 : 128;
   const int T = (((CFG ? g.Mh : g.M) + rpt - 1) / rpt) * ((g.N + 16 * NB - 1) / (16 * NB));
-  if (g_cus <= 0) {
-    int dev = 0, cus = 0;
-    hipError_t e = hipGetDevice(&dev);
-    if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
-    if (e != hipSuccess) return e;
-    g_cus = cus;
-  }
-  const int G = T < g_cus ? T : g_cus;
+  int cus = 0;
+  const hipError_t e = device_cus(cus);
+  if (e != hipSuccess) return e;
+  const int G = T < cus ? T : cus;
   hipLaunchKernelGGL((k2_gemm<A4, SYM, CFG, HS, KS, NB>), dim3(G), dim3(kThreads), 0, s, g);
   return hipGetLastError();
 }
