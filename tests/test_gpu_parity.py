@@ -598,6 +598,37 @@ def test_graph_capture_replays(torch):
         assert torch.equal(y_graph.view(torch.int32), Y.view(torch.int32)), i
 
 
+def test_plan_lifecycle_releases_memory(torch):
+    # Plans and views of every kind (single Hadamard, input branches, weight
+    # views destroyed before and after their base) give back all their
+    # device memory.
+    from bit_post_quantization_amd import QuantLinear
+    W = _dev(torch, synth.weight_normal(29, "life/W", 384, 512))
+
+    def cycle():
+        a = QuantLinear(W, w_bits=4, a_bits=4, hadamard_block=128, a_scale="symmetric",
+                        single_hadamard=True)
+        b = QuantLinear(W, k_seg_offsets=[0, 256, 512])
+        c = QuantLinear(W)
+        va, vb, vc = a.lsb_view(1), b.lsb_view(2), c.lsb_view(3)
+        vc.update_lsb(1)
+        a.plan.destroy()      # base before its view
+        va.plan.destroy()
+        vb.plan.destroy()     # view before its base
+        b.plan.destroy()
+        c.plan.destroy()
+        vc.plan.destroy()
+
+    cycle()
+    torch.cuda.synchronize()
+    free0 = torch.cuda.mem_get_info()[0]
+    for _ in range(20):
+        cycle()
+    torch.cuda.synchronize()
+    free1 = torch.cuda.mem_get_info()[0]
+    assert abs(free1 - free0) < (8 << 20), (free0, free1)
+
+
 def test_cfg_combine_standalone(torch):
     from bit_post_quantization_amd import qlinear_cfg_combine
     for M, N in [(302, 77), (2, 1), (4096, 1152)]:
