@@ -868,8 +868,9 @@ __global__ __launch_bounds__(kThreads, 1) void k2_gemm(GemmArgs g) {
   static_assert(kStages == 4, "one LDS object per stage");
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // uniform
-  // waves w < NB - 8 also move weight pair w + 8 (NB is 8 or 9)
-  static_assert(NB == 8 || NB == 9, "wave roles");
+  // waves w < NB - 8 also move weight pair w + 8; with NB <= 12 those are
+  // all column-group-0 waves
+  static_assert(NB >= 8 && NB <= 12, "wave roles");
   if (wave < NB - 8)
     gemm_wave<A4, SYM, CFG, HS, KS, NB, 0, true>(g, wave, lane, st0, st1, st2, st3);
   else if (wave < 4)
@@ -919,10 +920,21 @@ hipError_t run_nb(const GemmArgs& g, hipStream_t s) {
 
 template <bool A4>
 hipError_t run_mode(const GemmArgs& g, int sym, int cfg, int hs, hipStream_t s) {
-  // Single Hadamard: symmetric codes, 128 weight rows (64 channels) per tile
-  // so that every wave holds whole hi/lo pairs.
+  // Single Hadamard: symmetric codes, 128 or 192 weight rows (64 or 96
+  // channels) per tile, so that every wave holds whole hi/lo pairs. The
+  // wider tile reads fewer LDS bytes per product; it is taken unless it
+  // needs more rounds of tiles over the compute units (in tile-width units).
   if (hs) {
     if (!sym || g.nks > 1) return hipErrorInvalidValue;
+    int cus = 0;
+    const hipError_t e = device_cus(cus);
+    if (e != hipSuccess) return e;
+    const long rows = ((cfg ? g.Mh : g.M) + (cfg ? 63 : 127)) / (cfg ? 64 : 128);
+    const long t8 = rows * ((g.N + 127) / 128), t12 = rows * ((g.N + 191) / 192);
+    const bool wide = ((t12 + cus - 1) / cus) * 12 <= ((t8 + cus - 1) / cus) * 8;
+    if (wide)
+      return cfg ? run<A4, true, true, true, false, 12>(g, s)
+                 : run<A4, true, false, true, false, 12>(g, s);
     return cfg ? run<A4, true, true, true, false, 8>(g, s)
                : run<A4, true, false, true, false, 8>(g, s);
   }

@@ -310,6 +310,17 @@ def test_single_hadamard(torch, M, K, N, B, w_bits, a_bits, cfg):
                  tag="single")
 
 
+@pytest.mark.parametrize("M,K,N,a_bits,cfg", [(4096, 256, 1152, 8, 1), (4096, 512, 1530, 4, 0)])
+def test_single_hadamard_wide_tiles(torch, M, K, N, a_bits, cfg):
+    # Shapes whose tile count makes the launcher pick 192-row (96-channel)
+    # tiles; the 8-bit case fills the whole 160 KB of LDS.
+    X = synth.gelu_with_outliers(30, f"single/wide/{M}{K}{N}", M, K)
+    W = synth.weight_normal(30, f"single/wide/W{M}{K}{N}", N, K)
+    rows = sample_rows(M, bool(cfg), 32, seed=7)
+    check_single(torch, X, W, M=M, K=K, N=N, B=128, w_bits=8, a_bits=a_bits, cfg=cfg, rows=rows,
+                 tag="wide")
+
+
 def test_single_hadamard_extremes(torch):
     # A bent sign pattern b of 64 entries (the inner product of the two 3-bit
     # halves of the index) has a flat transform: |H b| = 8 everywhere. Rows
