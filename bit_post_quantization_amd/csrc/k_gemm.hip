@@ -44,7 +44,9 @@
 //  * Single Hadamard (HQ-DM explainer 2.1, activations rotated only): the
 //    plan's weight rows hold hi and lo int8 planes of H W_int^T in adjacent
 //    16-row fragments; the symmetric kernel multiplies both and the epilogue
-//    combines each pair exactly in fp64 (epilogue_hs).
+//    combines each pair exactly in fp64 (epilogue_hs). Its tiles are 128 or
+//    192 weight rows (NB = 8 or 12; 192 uses all 160 KB of LDS with 8-bit
+//    activations).
 //  * Input branches (SegQuant explainer 2.A, input segmentation): when the
 //    K loop crosses a branch end, the branch's epilogue part is folded into
 //    fp32 partial sums held in a per-thread workspace slice and the
