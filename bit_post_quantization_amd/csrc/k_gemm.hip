@@ -913,10 +913,31 @@ hipError_t run(const GemmArgs& g, hipStream_t s) {
   return hipGetLastError();
 }
 
+// Whether 192-column tiles (NB = 12) beat tiles of 16 * nb columns: they
+// read fewer LDS bytes per product, and win unless they need more rounds of
+// tiles over the compute units, counted in tile-width units (ties go wide).
+hipError_t wide_tiles(const GemmArgs& g, int cfg, int nb, bool& wide) {
+  int cus = 0;
+  const hipError_t e = device_cus(cus);
+  if (e != hipSuccess) return e;
+  const long rows = ((cfg ? g.Mh : g.M) + (cfg ? 63 : 127)) / (cfg ? 64 : 128);
+  const long tn = rows * ((g.N + 16 * nb - 1) / (16 * nb)), t12 = rows * ((g.N + 191) / 192);
+  wide = ((t12 + cus - 1) / cus) * 12 <= ((tn + cus - 1) / cus) * nb;
+  return hipSuccess;
+}
+
 template <bool A4, bool SYM, bool CFG>
 hipError_t run_nb(const GemmArgs& g, hipStream_t s) {
-  // 144-column tiles when they divide N, else 128.
-  if (g.N % 144 == 0) return run<A4, SYM, CFG, false, false, 9>(g, s);
+  // 144-column tiles when they divide N, else 128. The symmetric kernel
+  // (one accumulator set) has the registers for 192-column tiles too.
+  const int nb = g.N % 144 == 0 ? 9 : 8;
+  if constexpr (SYM) {
+    bool wide = false;
+    const hipError_t e = wide_tiles(g, CFG, nb, wide);
+    if (e != hipSuccess) return e;
+    if (wide) return run<A4, SYM, CFG, false, false, 12>(g, s);
+  }
+  if (nb == 9) return run<A4, SYM, CFG, false, false, 9>(g, s);
   return run<A4, SYM, CFG, false, false, 8>(g, s);
 }
 
@@ -928,12 +949,9 @@ hipError_t run_mode(const GemmArgs& g, int sym, int cfg, int hs, hipStream_t s) 
   // needs more rounds of tiles over the compute units (in tile-width units).
   if (hs) {
     if (!sym || g.nks > 1) return hipErrorInvalidValue;
-    int cus = 0;
-    const hipError_t e = device_cus(cus);
+    bool wide = false;
+    const hipError_t e = wide_tiles(g, cfg, 8, wide);
     if (e != hipSuccess) return e;
-    const long rows = ((cfg ? g.Mh : g.M) + (cfg ? 63 : 127)) / (cfg ? 64 : 128);
-    const long t8 = rows * ((g.N + 127) / 128), t12 = rows * ((g.N + 191) / 192);
-    const bool wide = ((t12 + cus - 1) / cus) * 12 <= ((t8 + cus - 1) / cus) * 8;
     if (wide)
       return cfg ? run<A4, true, true, true, false, 12>(g, s)
                  : run<A4, true, false, true, false, 12>(g, s);

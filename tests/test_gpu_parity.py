@@ -321,6 +321,17 @@ def test_single_hadamard_wide_tiles(torch, M, K, N, a_bits, cfg):
                  tag="wide")
 
 
+@pytest.mark.parametrize("M,K,N,a_bits,cfg", [(4096, 256, 4608, 8, 1), (4096, 512, 1530, 4, 0)])
+def test_symmetric_wide_tiles(torch, M, K, N, a_bits, cfg):
+    # Symmetric activations at shapes whose tile count makes the launcher
+    # pick 192-column tiles.
+    X = synth.gelu_with_outliers(31, f"sym/wide/{M}{K}{N}", M, K)
+    W = synth.weight_normal(31, f"sym/wide/W{M}{K}{N}", N, K)
+    rows = sample_rows(M, bool(cfg), 32, seed=8)
+    check_layer(torch, X, W, M=M, K=K, N=N, a_bits=a_bits, w_bits=8, B=128, a_scale="symmetric",
+                cfg=cfg, rows=rows, tag="sym-wide")
+
+
 def test_single_hadamard_extremes(torch):
     # A bent sign pattern b of 64 entries (the inner product of the two 3-bit
     # halves of the index) has a flat transform: |H b| = 8 everywhere. Rows
