@@ -96,11 +96,15 @@ class Layer:
         self.scales = torch.empty(2 * nks, dtype=torch.float32, device="cuda")
         rows = self.M // 2 if L.cfg else self.M
         self.Y = torch.empty((rows, L.N), dtype=torch.float32, device="cuda")
-        # algorithmic work
-        # MFMA work executed: two products per output with DualScale (both
-        # polarity planes) or with the single Hadamard (hi and lo planes).
-        planes = 2 if (L.a_scale == "dual" or L.single_hadamard) else 1
+        # Algorithmic work: two contractions per output with DualScale (both
+        # polarity planes, 4*M*N*K int ops), one with symmetric codes. The
+        # single Hadamard is one symmetric contraction of the method; the
+        # kernel executes it as two int8 products (hi and lo weight planes),
+        # reported apart as executed MFMA work.
+        planes = 2 if L.a_scale == "dual" else 1
         self.mfma_ops = planes * 2.0 * self.M * L.N * L.K
+        self.exec_ops = (2 if (L.a_scale == "dual" or L.single_hadamard) else 1) \
+            * 2.0 * self.M * L.N * L.K
         self.eff_ops = 2.0 * self.M * L.N * L.K
         xbytes = 2 if L.x_dtype == "bf16" else 4
         self.quant_bytes = self.M * L.K * (xbytes + L.a_bits / 8.0)
@@ -149,44 +153,113 @@ def bops_report(Ls, M):
             "mean_a_bits_by_macs": round(guided / (4 * sum(macs)), 3)}
 
 
-def cpu_baseline(layers, budget_s):
+def host_info():
+    """CPU model and core counts of the machine the oracle runs on."""
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return {"cpu_model": model, "nproc": os.cpu_count(),
+            "cores_allowed": len(os.sched_getaffinity(0))}
+
+
+def _oracle_rows(oracle, ly, codes, s, wp, rows):
+    """GEMM + epilogue (+ CFG) of the oracle on a list of output rows
+    (conditional rows with CFG: each is paired with its unconditional row)."""
+    L = ly.L
+    half = ly.M // 2
+    for n in rows:
+        r = np.array([n, n + half]) if L.cfg else np.array([n])
+        y, _, _ = oracle.linear_rows(codes, s, wp, r, L.a_scale)
+        if L.cfg:
+            oracle.cfg_combine(y[:1], y[1:], L.guidance)
+
+
+def cpu_baseline(layers, budget_s, threads=None):
     """The oracle, as it stands, on a bounded sample of the same workload:
     every activation code of every layer, and the GEMM + epilogue (+ CFG) on
-    row pairs until the time budget is spent; scaled to the whole step."""
+    row pairs until the time budget is spent; scaled to the whole step.
+    The timed thread is pinned to one host core. A secondary figure runs P
+    threads, each the same single-threaded oracle on a disjoint shard of the
+    rows (the library releases the interpreter lock while it computes)."""
+    import concurrent.futures as cf
     import oracle
-    t_quant = 0.0
-    t_gemm_per_row = []
-    rows_done = []
-    per_layer_budget = budget_s / max(1, len(layers))
-    for ly in layers:
-        L = ly.L
-        t0 = time.perf_counter()
-        x = oracle.bf16_to_f32(ly.X_host) if L.x_dtype == "bf16" else ly.X_host
-        codes, s = oracle.quantize_activations(x, L.a_bits, B=L.hadamard_block, mode=L.a_scale)
-        t_quant += time.perf_counter() - t0
-        wp = oracle.WeightPlan(ly.W_host, L.w_bits, B=L.hadamard_block, mode=L.w_scale,
-                               seg_offsets=None if L.seg_offsets() is None else L.seg_offsets())
-        half = ly.M // 2
-        n = 0
-        t0 = time.perf_counter()
-        while True:
-            r = np.array([n, n + half]) if L.cfg else np.array([n])
-            y, _, _ = oracle.linear_rows(codes, s, wp, r, L.a_scale)
-            if L.cfg:
-                oracle.cfg_combine(y[:1], y[1:], L.guidance)
-            n += 1
-            el = time.perf_counter() - t0
-            if (el > per_layer_budget and n >= 2) or n >= (half if L.cfg else ly.M):
-                break
-        rows_done.append(n * (2 if L.cfg else 1))
-        t_gemm_per_row.append(el / (n * (2 if L.cfg else 1)))
+    allowed = sorted(os.sched_getaffinity(0))
+    os.sched_setaffinity(0, {allowed[0]})
+    try:
+        t_quant = 0.0
+        t_gemm_per_row = []
+        rows_done = []
+        prepared = []
+        per_layer_budget = budget_s / max(1, len(layers))
+        for ly in layers:
+            L = ly.L
+            t0 = time.perf_counter()
+            x = oracle.bf16_to_f32(ly.X_host) if L.x_dtype == "bf16" else ly.X_host
+            codes, s = oracle.quantize_activations(x, L.a_bits, B=L.hadamard_block, mode=L.a_scale)
+            t_quant += time.perf_counter() - t0
+            wp = oracle.WeightPlan(ly.W_host, L.w_bits, B=L.hadamard_block, mode=L.w_scale,
+                                   seg_offsets=None if L.seg_offsets() is None else L.seg_offsets())
+            prepared.append((codes, s, wp))
+            top = ly.M // 2 if L.cfg else ly.M
+            n = 0
+            t0 = time.perf_counter()
+            while True:
+                _oracle_rows(oracle, ly, codes, s, wp, [n])
+                n += 1
+                el = time.perf_counter() - t0
+                if (el > per_layer_budget and n >= 2) or n >= top:
+                    break
+            per = 2 if L.cfg else 1
+            rows_done.append(n * per)
+            t_gemm_per_row.append(el / (n * per))
+    finally:
+        os.sched_setaffinity(0, set(allowed))
     t_step = t_quant + sum(t * ly.M for t, ly in zip(t_gemm_per_row, layers))
     ops = sum(ly.mfma_ops for ly in layers)
     sample = ("full activation quantization of every layer; GEMM+epilogue+CFG on "
               + ", ".join(f"{r} of {ly.M} rows ({ly.L.name})" for r, ly in zip(rows_done, layers))
               + "; step time extrapolated linearly in rows")
-    return {"value": ops / t_step / 1e12, "unit": "TOPS", "cores": 1, "kind": "oracle",
-            "sample": sample, "step_seconds_extrapolated": t_step}
+    out = {"value": ops / t_step / 1e12, "unit": "TOPS", "cores": 1, "kind": "oracle",
+           "sample": sample, "step_seconds_extrapolated": t_step,
+           "host": {**host_info(), "pinned_to_core": allowed[0]}}
+    # Secondary figure: P threads, each the single-threaded oracle on its own
+    # shard of the output rows (GEMM + epilogue + CFG), for a fixed wall time.
+    P = threads or min(16, len(allowed))
+    wall = max(1.0, budget_s / 3.0)
+    done_rows = []
+    t_wall = []
+    for ly, (codes, s, wp) in zip(layers, prepared):
+        top = ly.M // 2 if ly.L.cfg else ly.M
+        shards = np.array_split(np.arange(top), P)
+        stop = time.perf_counter() + wall / max(1, len(layers))
+
+        def work(rows, ly=ly, codes=codes, s=s, wp=wp, stop=stop):
+            cnt = 0
+            for n in rows:
+                _oracle_rows(oracle, ly, codes, s, wp, [int(n)])
+                cnt += 1
+                if time.perf_counter() > stop:
+                    break
+            return cnt
+
+        t0 = time.perf_counter()
+        with cf.ThreadPoolExecutor(max_workers=P) as ex:
+            cnt = sum(ex.map(work, shards))
+        t_wall.append(time.perf_counter() - t0)
+        done_rows.append(cnt * (2 if ly.L.cfg else 1))
+    t_step_p = t_quant + sum(t / r * ly.M for t, r, ly in zip(t_wall, done_rows, layers))
+    out["parallel"] = {"threads": P, "value": ops / t_step_p / 1e12, "unit": "TOPS",
+                       "sample": "GEMM+epilogue+CFG on " + ", ".join(
+                           f"{r} rows ({ly.L.name})" for r, ly in zip(done_rows, layers))
+                       + " over P disjoint row shards; quantization at the single-thread time; "
+                         "scaled linearly in rows"}
+    return out
 
 
 COPY_BYTES = 512 << 20      # calibration copy: 512 MiB read + 512 MiB written per copy
@@ -560,25 +633,54 @@ def main():
     q_ms /= args.steps
     g_ms /= args.steps
 
+    # Timed region 3: per layer, `steps` launches of the same call back to
+    # back between one event pair (launch-to-launch time: the kernel plus the
+    # gap between dependent dispatches, without per-launch event overhead).
+    # These durations feed the rooflines.
+    def back_to_back(fn):
+        a, b = ev(), ev()
+        torch.cuda.synchronize()
+        a.record()
+        for _ in range(args.steps):
+            fn()
+        b.record()
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / args.steps
+    qb_ms = np.array([back_to_back(ly.quantize) for ly in layers])
+    gb_ms = np.array([back_to_back(ly.gemm) for ly in layers])
+
     step_ops = sum(ly.mfma_ops for ly in layers)
     value = step_ops / (ms_step * 1e-3) / 1e12
     # dominant kernel: the GEMM (k2), averaged over its launches in the step
-    gemm_avg_s = float(np.mean(g_ms)) * 1e-3
+    gemm_avg_s = float(np.mean(gb_ms)) * 1e-3
     ops_per_launch = float(np.mean([ly.mfma_ops for ly in layers]))
     gemm_tops = ops_per_launch / gemm_avg_s / 1e12
     qbytes = sum(ly.quant_bytes for ly in layers)
-    q_gbps = qbytes / (float(np.sum(q_ms)) * 1e-3) / 1e9
+    q_gbps = qbytes / (float(np.sum(qb_ms)) * 1e-3) / 1e9
 
     per_layer = []
-    for ly, q, g in zip(layers, q_ms, g_ms):
+    for ly, q, g, qb, gb in zip(layers, q_ms, g_ms, qb_ms, gb_ms):
         per_layer.append({
             "layer": ly.L.name, "M": ly.M, "K": ly.L.K, "N": ly.L.N,
-            "quant_us": round(q * 1e3, 2),
-            "quant_gbps": round(ly.quant_bytes / (q * 1e-3) / 1e9, 1),
-            "gemm_us": round(g * 1e3, 2),
-            "gemm_mfma_tops": round(ly.mfma_ops / (g * 1e-3) / 1e12, 1),
-            "gemm_frac_int8_peak": round(ly.mfma_ops / (g * 1e-3) / 1e12 / PEAK_INT8_TOPS, 4),
+            "quant_us": round(qb * 1e3, 2), "quant_us_in_step_event_pair": round(q * 1e3, 2),
+            "quant_gbps": round(ly.quant_bytes / (qb * 1e-3) / 1e9, 1),
+            "gemm_us": round(gb * 1e3, 2), "gemm_us_in_step_event_pair": round(g * 1e3, 2),
+            "gemm_tops": round(ly.mfma_ops / (gb * 1e-3) / 1e12, 1),
+            "gemm_frac_int8_peak": round(ly.mfma_ops / (gb * 1e-3) / 1e12 / PEAK_INT8_TOPS, 4),
+            "gemm_executed_mfma_tops": round(ly.exec_ops / (gb * 1e-3) / 1e12, 1),
         })
+
+    # K3, the standalone CFG combine, on the first layer's full output shape
+    # (both halves of Y [M, N] in, [M/2, N] out): 12 bytes per output element.
+    from bit_post_quantization_amd import qlinear_cfg_combine
+    ly0 = layers[0]
+    Yfull = torch.empty((ly0.M, ly0.L.N), dtype=torch.float32, device="cuda").normal_()
+    Yc = torch.empty((ly0.M // 2, ly0.L.N), dtype=torch.float32, device="cuda")
+    k3 = lambda: qlinear_cfg_combine(Yfull, ly0.M, ly0.L.N, 4.0, Yc)  # noqa: E731
+    k3()
+    k3_ms = back_to_back(k3)
+    k3_bytes = 12.0 * (ly0.M // 2) * ly0.L.N
+    del Yfull, Yc
 
     first = wl.layers[0] if args.workload != "mlp" else Ls[0]
     out = {
@@ -618,6 +720,8 @@ def main():
             "bound": "mfma", "achieved": round(gemm_tops, 1), "peak": PEAK_INT8_TOPS,
             "unit": "TOPS", "frac": round(gemm_tops / PEAK_INT8_TOPS, 4),
             "ops_per_launch": ops_per_launch, "avg_launch_us": round(gemm_avg_s * 1e6, 2),
+            "timing": "launch-to-launch time of back-to-back launches of each layer's GEMM "
+                      "(HIP events on the launching stream), averaged over the layers",
             "traffic": measured_traffic() if args.workload == "mlp" else None,
         },
         "act_quant": {
@@ -625,8 +729,17 @@ def main():
             "achieved": round(q_gbps, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
             "frac": round(q_gbps / PEAK_HBM_GBPS, 4),
             "bytes_per_step": qbytes,
+            "timing": "launch-to-launch time of back-to-back quantize calls per layer",
+        },
+        "cfg_combine": {
+            "kernel": "k3_cfg (standalone CFG combine)", "bound": "hbm",
+            "shape": [ly0.M, ly0.L.N], "bytes_per_launch": k3_bytes,
+            "avg_launch_us": round(k3_ms * 1e3, 2),
+            "achieved": round(k3_bytes / (k3_ms * 1e-3) / 1e9, 1), "peak": PEAK_HBM_GBPS,
+            "unit": "GB/s", "frac": round(k3_bytes / (k3_ms * 1e-3) / 1e9 / PEAK_HBM_GBPS, 4),
         },
         "effective_tops": round(sum(ly.eff_ops for ly in layers) / (ms_step * 1e-3) / 1e12, 2),
+        "executed_mfma_tops": round(sum(ly.exec_ops for ly in layers) / (ms_step * 1e-3) / 1e12, 2),
         "layers": per_layer,
         "wall_s": round(wall, 3),
     }

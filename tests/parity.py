@@ -13,6 +13,8 @@ stage is checked on its own inputs.
 """
 from __future__ import annotations
 
+import concurrent.futures as cf
+import os
 import sys
 
 import numpy as np
@@ -88,3 +90,35 @@ def assert_close(gpu: np.ndarray, ref: np.ndarray, what: str):
     e = rel_err(gpu, ref)
     assert e <= Y_REL_TOL, f"{what}: max rel err {e}"
     return e
+
+
+def oracle_threads() -> int:
+    """Worker threads for running the single-threaded oracle on disjoint row
+    shards (at most 16: the CPU share of one GPU on the test hosts)."""
+    return max(1, min(16, len(os.sched_getaffinity(0))))
+
+
+def _sharded(fn, rows, *args):
+    rows = np.ascontiguousarray(rows, dtype=np.int64)
+    P = oracle_threads()
+    shards = [r for r in np.array_split(rows, P) if r.size]
+    if len(shards) <= 1:
+        return [fn(*args, rows)]
+    with cf.ThreadPoolExecutor(max_workers=len(shards)) as ex:
+        return list(ex.map(lambda r: fn(*args, r), shards))
+
+
+def gemm_dual_rows(codes: np.ndarray, wc: np.ndarray, rows) -> tuple:
+    """oracle.gemm_dual over the listed rows, the rows split into shards that
+    independent threads run through the (single-threaded) oracle; the oracle
+    releases the interpreter lock while it computes."""
+    parts = _sharded(oracle.gemm_dual, rows, np.ascontiguousarray(codes, dtype=np.int8),
+                     np.ascontiguousarray(wc, dtype=np.int8))
+    return (np.concatenate([p[0] for p in parts]), np.concatenate([p[1] for p in parts]))
+
+
+def gemm_int64_rows(codes: np.ndarray, v: np.ndarray, rows) -> np.ndarray:
+    """oracle.gemm_int64 over the listed rows, sharded over threads as above."""
+    parts = _sharded(oracle.gemm_int64, rows, np.ascontiguousarray(codes, dtype=np.int8),
+                     np.ascontiguousarray(v, dtype=np.int32))
+    return np.concatenate(parts)

@@ -7,8 +7,8 @@ import numpy as np
 import pytest
 
 import oracle
-from tests.parity import (assert_close, assert_codes, compare_codes, compare_codes_scaled, say,
-                          unpack_codes)
+from tests.parity import (assert_close, assert_codes, compare_codes, compare_codes_scaled,
+                          gemm_dual_rows, gemm_int64_rows, say, unpack_codes)
 from workloads import configs, synth
 
 pytestmark = pytest.mark.gpu
@@ -96,7 +96,7 @@ def check_layer(torch, X, W, *, M, K, N, w_bits=8, a_bits=8, B=0, seg=None, w_sc
     accp_g = dbg[0].index_select(0, idx).cpu().numpy()
     accn_g = dbg[1].index_select(0, idx).cpu().numpy()
     Y_g = Yd.index_select(0, torch.from_numpy(out_rows).cuda()).cpu().numpy()
-    accp_o, accn_o = oracle.gemm_dual(codes_g, wp.codes, acc_rows)
+    accp_o, accn_o = gemm_dual_rows(codes_g, wp.codes, acc_rows)
     if a_scale == "symmetric":
         assert np.array_equal(accp_g.astype(np.int64), accp_o.astype(np.int64) + accn_o), "acc (sym)"
         assert not accn_g.any()
@@ -157,7 +157,7 @@ def check_single(torch, X, W, *, M, K, N, B, w_bits=8, a_bits=8, cfg=0, guidance
     idx = torch.from_numpy(acc_rows).cuda()
     hi = dbg[0].index_select(0, idx).cpu().numpy().astype(np.int64)
     lo = dbg[1].index_select(0, idx).cpu().numpy().astype(np.int64)
-    acc_o = oracle.gemm_int64(codes_g, wp.v, acc_rows)
+    acc_o = gemm_int64_rows(codes_g, wp.v, acc_rows)
     assert np.array_equal(128 * hi + lo, acc_o), "exact accumulators"
     y_o = oracle.epilogue_single(acc_o, s_g[0], wp.scales, B)
     if cfg:
@@ -683,11 +683,13 @@ def test_gpu_argument_errors(torch):
 # ------------------------------------------------------------ full size ----
 
 def _run_workload_layer(torch, key, li, rows_n=48):
+    """One layer of a workload at full size; rows_n=None checks every
+    output row (the oracle GEMM sharded over threads)."""
     wl = configs.WORKLOADS[key]
     L = wl.layers[li]
     X = configs.make_x(wl, L)
     W = configs.make_w(wl, L)
-    rows = sample_rows(wl.M, L.cfg, rows_n, seed=li)
+    rows = None if rows_n is None else sample_rows(wl.M, L.cfg, rows_n, seed=li)
     return check_layer(torch, X, W, M=wl.M, K=L.K, N=L.N, w_bits=L.w_bits, a_bits=L.a_bits,
                        B=L.hadamard_block, seg=None if L.seg_offsets() is None else L.seg_offsets().tolist(),
                        w_scale=L.w_scale, a_scale=L.a_scale, x_dtype=L.x_dtype, cfg=int(L.cfg),
@@ -697,13 +699,13 @@ def _run_workload_layer(torch, key, li, rows_n=48):
 @pytest.mark.timeout(600)
 @pytest.mark.parametrize("li", range(4))
 def test_config2_dit_w8a8_cfg(torch, li):
-    _run_workload_layer(torch, "c2", li)
+    _run_workload_layer(torch, "c2", li, rows_n=None)
 
 
 @pytest.mark.timeout(600)
 @pytest.mark.parametrize("li", range(4))
 def test_config3_dit_w4a4_hadamard(torch, li):
-    _run_workload_layer(torch, "c3", li)
+    _run_workload_layer(torch, "c3", li, rows_n=None)
 
 
 @pytest.mark.timeout(600)
@@ -713,9 +715,8 @@ def test_config3_single_hadamard(torch, li):
     L = configs.c3_single()[li]
     X = configs.make_x(wl, L)
     W = configs.make_w(wl, L)
-    rows = sample_rows(wl.M, True, 48, seed=200 + li)
     check_single(torch, X, W, M=wl.M, K=L.K, N=L.N, B=L.hadamard_block, w_bits=L.w_bits,
-                 a_bits=L.a_bits, cfg=int(L.cfg), guidance=L.guidance, rows=rows,
+                 a_bits=L.a_bits, cfg=int(L.cfg), guidance=L.guidance, rows=None,
                  tag=f"c3s/{L.name}")
 
 
@@ -734,7 +735,7 @@ def test_config7_input_branches(torch, li):
 @pytest.mark.timeout(900)
 @pytest.mark.parametrize("li", range(4))
 def test_config4_mmdit_segments(torch, li):
-    _run_workload_layer(torch, "c4", li, rows_n=24)
+    _run_workload_layer(torch, "c4", li, rows_n=64)
 
 
 @pytest.mark.timeout(900)
