@@ -7,6 +7,7 @@
 
 #include <cstdarg>
 #include <cstdio>
+#include <mutex>
 #include <string>
 #include <vector>
 
@@ -180,6 +181,72 @@ ql_status enqueue_lsb(struct qlinear_plan* view, const struct qlinear_plan* base
     if (e != hipSuccess) return hip_fail(e, "single-Hadamard weight planes");
   }
   return QL_OK;
+}
+
+}  // namespace
+
+// Reduction workspace of qlinear_quantize_act_noalloc: one copy per device,
+// holding every partial maximum a call can write (kMaxKSeg branches x
+// kMaxReduceBlocks pairs, 32 KiB). Host code never passes `scratch` itself
+// to a kernel (that name is a host-side stand-in): it passes the device
+// address looked up once per device below.
+static __device__ __align__(256) uint8_t scratch[sizeof(ql::ReduceWs)];
+
+namespace {
+
+constexpr int kMaxScratchDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxScratchDevices] = {};
+
+// Device address of `scratch` on device `dev` (the current device), looked
+// up on the first call there and kept.
+hipError_t scratch_address(int dev, void** out) {
+  if (dev < 0 || dev >= kMaxScratchDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* ptr = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (!ptr) return hipErrorInvalidSymbol;
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return hipSuccess;
+}
+
+// Shared body of qlinear_quantize_act and its no-allocation variant: `ws`
+// receives the per-block partial maxima of a dynamic-scale call.
+ql_status quantize_impl(qlinear_plan_t p, const void* X, int32_t M, int32_t lsb_k,
+                        const float* static_scales, void* codes, float* act_scales,
+                        ql::ReduceWs* ws, void* stream) {
+  if (M < 0) return fail(QL_ERR_ARG, "M = %d must be >= 0", M);
+  if (lsb_k < 0 || lsb_k >= p->d.a_bits)
+    return fail(QL_ERR_ARG, "lsb_k = %d must be in [0, %d)", lsb_k, p->d.a_bits);
+  if (M == 0) return ok();  // empty tensors may carry NULL data pointers
+  if (!X || !codes || !act_scales) return fail(QL_ERR_ARG, "X, codes or act_scales is NULL");
+  const bool bf16 = p->d.x_dtype == QL_BF16;
+  if (!aligned(X, bf16 ? 8 : 16)) return fail(QL_ERR_ARG, "X is not %d-byte aligned", bf16 ? 8 : 16);
+  if (!aligned(codes, 16)) return fail(QL_ERR_ARG, "codes must be 16-byte aligned");
+  if (!aligned(act_scales, 4) || (static_scales && !aligned(static_scales, 4)))
+    return fail(QL_ERR_ARG, "scale pointers must be 4-byte aligned");
+  ql::QuantArgs a;
+  a.X = X;
+  a.nunits = (int64_t)M * p->d.K / 4;
+  a.codes = codes;
+  a.act_scales = act_scales;
+  a.static_scales = static_scales;
+  a.ws = ws;
+  a.reduce_blocks = 0;
+  a.qa = (float)qmax(p->d.a_bits);
+  a.keep_mask = ~((1 << lsb_k) - 1);
+  a.sym = p->d.a_scale_mode == QL_ASCALE_SYMMETRIC;
+  a.nks = p->nks;
+  a.k_units = p->d.K / 4;
+  for (int j = 0; j < ql::kMaxKSeg; ++j) a.ks_units[j] = j < p->nks ? p->kseg[j] / 4 : a.k_units;
+  hipError_t e = ql::launch_quantize(a, bf16, p->d.hadamard_block, p->d.a_bits == 4,
+                                     reinterpret_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "launching quantize");
+  return ok();
 }
 
 }  // namespace
@@ -390,34 +457,24 @@ ql_status qlinear_quantize_act(qlinear_plan_t p, const void* X, int32_t M, int32
                                void* stream) {
   ql_status st = check_plan(p);
   if (st != QL_OK) return st;
-  if (M < 0) return fail(QL_ERR_ARG, "M = %d must be >= 0", M);
-  if (lsb_k < 0 || lsb_k >= p->d.a_bits)
-    return fail(QL_ERR_ARG, "lsb_k = %d must be in [0, %d)", lsb_k, p->d.a_bits);
-  if (M == 0) return ok();  // empty tensors may carry NULL data pointers
-  if (!X || !codes || !act_scales) return fail(QL_ERR_ARG, "X, codes or act_scales is NULL");
-  const bool bf16 = p->d.x_dtype == QL_BF16;
-  if (!aligned(X, bf16 ? 8 : 16)) return fail(QL_ERR_ARG, "X is not %d-byte aligned", bf16 ? 8 : 16);
-  if (!aligned(codes, 16)) return fail(QL_ERR_ARG, "codes must be 16-byte aligned");
-  if (!aligned(act_scales, 4) || (static_scales && !aligned(static_scales, 4)))
-    return fail(QL_ERR_ARG, "scale pointers must be 4-byte aligned");
-  ql::QuantArgs a;
-  a.X = X;
-  a.nunits = (int64_t)M * p->d.K / 4;
-  a.codes = codes;
-  a.act_scales = act_scales;
-  a.static_scales = static_scales;
-  a.ws = p->ws;
-  a.reduce_blocks = 0;
-  a.qa = (float)qmax(p->d.a_bits);
-  a.keep_mask = ~((1 << lsb_k) - 1);
-  a.sym = p->d.a_scale_mode == QL_ASCALE_SYMMETRIC;
-  a.nks = p->nks;
-  a.k_units = p->d.K / 4;
-  for (int j = 0; j < ql::kMaxKSeg; ++j) a.ks_units[j] = j < p->nks ? p->kseg[j] / 4 : a.k_units;
-  hipError_t e = ql::launch_quantize(a, bf16, p->d.hadamard_block, p->d.a_bits == 4,
-                                     reinterpret_cast<hipStream_t>(stream));
-  if (e != hipSuccess) return hip_fail(e, "launching quantize");
-  return ok();
+  return quantize_impl(p, X, M, lsb_k, static_scales, codes, act_scales, p->ws, stream);
+}
+
+ql_status qlinear_quantize_act_noalloc(qlinear_plan_t p, const void* X, int32_t M,
+                                       int32_t lsb_k, const float* static_scales, void* codes,
+                                       float* act_scales, void* stream) {
+  ql_status st = check_plan(p);
+  if (st != QL_OK) return st;
+  // The scratch holds kMaxKSeg branches of kMaxReduceBlocks partial pairs;
+  // the reduce grid never exceeds kMaxReduceBlocks blocks, whatever M.
+  if (p->nks > ql::kMaxKSeg)
+    return fail(QL_ERR_UNSUPPORTED, "%d input branches exceed the scratch's %d", p->nks,
+                ql::kMaxKSeg);
+  void* ws = nullptr;
+  const hipError_t e = scratch_address(p->device, &ws);
+  if (e != hipSuccess) return hip_fail(e, "looking up the reduction scratch");
+  return quantize_impl(p, X, M, lsb_k, static_scales, codes, act_scales,
+                       reinterpret_cast<ql::ReduceWs*>(ws), stream);
 }
 
 ql_status qlinear_gemm(qlinear_plan_t p, const void* codes, const float* act_scales, int32_t M,

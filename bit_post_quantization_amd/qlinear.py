@@ -114,6 +114,13 @@ def qlinear_quantize_act(plan: Plan, X, M: int, lsb_k: int, static_scales, codes
                                            _ptr(codes), _ptr(act_scales), _stream(stream)))
 
 
+def qlinear_quantize_act_noalloc(plan: Plan, X, M: int, lsb_k: int, static_scales, codes,
+                                 act_scales, stream=None) -> None:
+    check(_lib.load().qlinear_quantize_act_noalloc(plan.handle, _ptr(X), M, lsb_k,
+                                                   _ptr(static_scales), _ptr(codes),
+                                                   _ptr(act_scales), _stream(stream)))
+
+
 def qlinear_gemm(plan: Plan, codes, act_scales, M: int, cfg: int, w: float, Y, acc_dbg=None,
                  stream=None) -> None:
     check(_lib.load().qlinear_gemm(plan.handle, _ptr(codes), _ptr(act_scales), M, cfg, float(w),

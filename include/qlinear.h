@@ -208,6 +208,26 @@ ql_status qlinear_quantize_act(qlinear_plan_t p, const void* X, int32_t M, int32
                                void* stream);
 
 /*
+ * For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): the same
+ * computation, arguments, results and errors as qlinear_quantize_act, but
+ * the per-block partial maxima of a dynamic-scale call go to a scratch array
+ * that the library keeps in device memory (32 KiB per device, reserved when
+ * the library is loaded, held until the process ends) instead of the plan's
+ * workspace. The scratch holds every partial a call writes (at most 1024 per
+ * input branch, whatever M), so no size is refused for its sake; a call
+ * never allocates, frees or synchronises. All calls on one device share its
+ * scratch: two such calls with dynamic scales that overlap in time on one
+ * device (different streams without ordering) race and give undefined
+ * codes; calls ordered on one stream are safe (each writes all the partials
+ * it reads). The first call on a device looks up the scratch's address
+ * there (host-side, no allocation).
+ */
+ql_status qlinear_quantize_act_noalloc(qlinear_plan_t p, const void* X, int32_t M,
+                                       int32_t lsb_k, const float* static_scales, void* codes,
+                                       float* act_scales, void* stream);
+
+/*
  * Integer GEMM of the codes against the plan's weight codes with the fp32
  * epilogue. DUAL: acc+ = sum_k max(c,0) w, acc- = sum_k min(c,0) w (int32,
  * exact), y = ((float)acc+ * s+ + (float)acc- * s-) * s_w[n];
