@@ -1,6 +1,8 @@
-// K2: integer GEMM of the activation codes against the weight codes on the
-// int8 matrix cores of gfx950, both DualScale polarity planes in one kernel,
-// with the fp32 epilogue (scales, Hadamard normalisation, CFG combine) fused.
+// K2 for the plans k_gemm1.hip does not take: HQ-DM's single Hadamard
+// (hi/lo weight planes) and SegLinear inputs of 3 or 4 branches. Integer
+// GEMM of the activation codes against the weight codes on the int8 matrix
+// cores of gfx950, both DualScale polarity planes in one kernel, with the
+// fp32 epilogue (scales, Hadamard normalisation, CFG combine) fused.
 //
 // Method (pages): SegQuant explainer 2.B -- X is split into its
 // non-negative and negative parts, each multiplied by the weight codes; the
@@ -35,9 +37,8 @@
 //    unpacked on the way into the MFMA, each code multiplied by 16 (nibble
 //    placed in the high half of its byte: two ANDs, a shift, two byte
 //    permutes); accumulators are shifted back exactly in the epilogue.
-//    4-bit weight codes arrive already expanded to one int8 per code (the
-//    plan stores them so): the kernel is bound by its MFMA and VALU issue,
-//    not by weight bytes, so the per-step weight unpack is not worth it.
+//    4-bit weight codes arrive expanded to one int8 per code (plans served
+//    here store them so).
 //  * CFG pairing: a row band is 16 conditional rows and their 16
 //    unconditional partners (fragments 0 and 1), so a lane holds both
 //    accumulators of a pair in the same register slot.
@@ -926,21 +927,6 @@ hipError_t wide_tiles(const GemmArgs& g, int cfg, int nb, bool& wide) {
   return hipSuccess;
 }
 
-template <bool A4, bool SYM, bool CFG>
-hipError_t run_nb(const GemmArgs& g, hipStream_t s) {
-  // 144-column tiles when they divide N, else 128. The symmetric kernel
-  // (one accumulator set) has the registers for 192-column tiles too.
-  const int nb = g.N % 144 == 0 ? 9 : 8;
-  if constexpr (SYM) {
-    bool wide = false;
-    const hipError_t e = wide_tiles(g, CFG, nb, wide);
-    if (e != hipSuccess) return e;
-    if (wide) return run<A4, SYM, CFG, false, false, 12>(g, s);
-  }
-  if (nb == 9) return run<A4, SYM, CFG, false, false, 9>(g, s);
-  return run<A4, SYM, CFG, false, false, 8>(g, s);
-}
-
 template <bool A4>
 hipError_t run_mode(const GemmArgs& g, int sym, int cfg, int hs, hipStream_t s) {
   // Single Hadamard: symmetric codes, 128 or 192 weight rows (64 or 96
@@ -958,16 +944,17 @@ hipError_t run_mode(const GemmArgs& g, int sym, int cfg, int hs, hipStream_t s) 
     return cfg ? run<A4, true, true, true, false, 8>(g, s)
                : run<A4, true, false, true, false, 8>(g, s);
   }
-  // Input branches: 128-column tiles (the partial sums take 32 registers).
-  if (g.nks > 1) {
+  // Three or four input branches: 128-column tiles (the partial sums take
+  // 32 registers).
+  if (g.nks > 2) {
     if (sym)
       return cfg ? run<A4, true, true, false, true, 8>(g, s)
                  : run<A4, true, false, false, true, 8>(g, s);
     return cfg ? run<A4, false, true, false, true, 8>(g, s)
                : run<A4, false, false, false, true, 8>(g, s);
   }
-  if (sym) return cfg ? run_nb<A4, true, true>(g, s) : run_nb<A4, true, false>(g, s);
-  return cfg ? run_nb<A4, false, true>(g, s) : run_nb<A4, false, false>(g, s);
+  // every other plan runs k_gemm1.hip
+  return hipErrorInvalidValue;
 }
 
 }  // namespace

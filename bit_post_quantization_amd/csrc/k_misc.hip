@@ -127,6 +127,39 @@ __global__ __launch_bounds__(256) void k0_truncate_w(const uint4* in, int64_t n1
                       truncate4(v.w, keep));
 }
 
+// 4-bit weight codes stored two per byte (the layout of the packed
+// activation codes: element 2i in the low nibble of byte i, element 2i + 1
+// in the high nibble); 16 codes per thread.
+__global__ __launch_bounds__(256) void k0_pack4(const uint4* in, int64_t n16, uint2* out) {
+  const int64_t u = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (u >= n16) return;
+  const uint4 v = in[u];
+  auto pk = [](uint32_t w) {  // 4 codes -> 2 bytes
+    return (w & 0xFu) | ((w >> 4) & 0xF0u) | ((w >> 8) & 0xF00u) | ((w >> 12) & 0xF000u);
+  };
+  out[u] = make_uint2(pk(v.x) | (pk(v.y) << 16), pk(v.z) | (pk(v.w) << 16));
+}
+
+// The inverse: int8 codes (sign-extended nibbles), the k low magnitude bits
+// cleared (keep = ~(2^k - 1)); 16 codes per thread.
+__global__ __launch_bounds__(256) void k0_unpack4(const uint2* in, int64_t n16, int32_t keep,
+                                                  uint4* out) {
+  const int64_t u = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (u >= n16) return;
+  const uint2 v = in[u];
+  auto up = [keep](uint32_t h) {  // 2 packed bytes -> 4 codes
+    uint32_t r = 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int c = (int)(int8_t)(uint8_t)(((h >> (4 * i)) & 0xFu) << 4) >> 4;
+      const int t = c >= 0 ? (c & keep) : -((-c) & keep);
+      r |= ((uint32_t)t & 0xFFu) << (8 * i);
+    }
+    return r;
+  };
+  out[u] = make_uint4(up(v.x & 0xFFFFu), up(v.x >> 16), up(v.y & 0xFFFFu), up(v.y >> 16));
+}
+
 // Single-Hadamard weights ([HQ-DM explainer 2.1: only the activations are
 // rotated]): V = H W_int^T row by row, exact (integers below 2^24 in fp32),
 // split into two int8 planes V = 128 * hi + lo with lo in [0, 127] and hi in
@@ -228,6 +261,25 @@ hipError_t launch_truncate_weights(const uint8_t* in, int64_t nbytes, int k, uin
   hipLaunchKernelGGL(k0_truncate_w, dim3(blocks_for(threads, 256)), dim3(256), 0, s,
                      reinterpret_cast<const uint4*>(in), n16, keep, reinterpret_cast<uint4*>(out),
                      sw_in, sw_out, nsw);
+  return hipGetLastError();
+}
+
+hipError_t launch_pack4(const uint8_t* codes, int64_t n, uint8_t* packed, hipStream_t s) {
+  if (n % 16 != 0) return hipErrorInvalidValue;
+  const int64_t n16 = n / 16;
+  if (n16 == 0) return hipSuccess;
+  hipLaunchKernelGGL(k0_pack4, dim3(blocks_for(n16, 256)), dim3(256), 0, s,
+                     reinterpret_cast<const uint4*>(codes), n16, reinterpret_cast<uint2*>(packed));
+  return hipGetLastError();
+}
+
+hipError_t launch_unpack4(const uint8_t* packed, int64_t n, int k, uint8_t* codes, hipStream_t s) {
+  if (n % 16 != 0 || k < 0 || k > 3) return hipErrorInvalidValue;
+  const int64_t n16 = n / 16;
+  if (n16 == 0) return hipSuccess;
+  hipLaunchKernelGGL(k0_unpack4, dim3(blocks_for(n16, 256)), dim3(256), 0, s,
+                     reinterpret_cast<const uint2*>(packed), n16, (int32_t)~((1 << k) - 1),
+                     reinterpret_cast<uint4*>(codes));
   return hipGetLastError();
 }
 

@@ -34,7 +34,7 @@ struct QuantArgs {
 
 struct GemmArgs {
   const uint8_t* A;          // activation codes: int8 [M,K] or packed [M,K/2]
-  const uint8_t* W;          // weight codes: int8 [N,K] (4-bit codes expanded)
+  const uint8_t* W;          // weight codes: int8 [N,K], or 4-bit packed [N,K/2]
   const float* act_scales;   // [2 * nks]
   const float* w_scales;     // [nks * Nout]
   float* Y;                  // [M,N] or [M/2,N]
@@ -48,6 +48,9 @@ struct GemmArgs {
   int nks;                   // input branches (1: none)
   int ks_end[kMaxKSeg];      // K-step (of 128) at which each branch but the last ends
   float* ypart_ws;           // input branches: kYSlots * kGemmThreads floats per workgroup
+  int kofs[kMaxKSeg + 1];    // branch j covers K columns [kofs[j], kofs[j+1])
+  int ksteps[kMaxKSeg];      // 128-column steps of branch j, rounded up to a multiple of 3
+  int w_lsb_k;               // TASQ: low magnitude bits cleared from every weight code
 };
 
 // GEMM workgroup size and the per-thread partial-sum slots of a GEMM with
@@ -64,9 +67,19 @@ hipError_t launch_quantize(const QuantArgs& a, int x_bf16, int hadamard_block, i
                            hipStream_t s);
 
 // K1 with input branches: launch_quantize handles a.nks > 1 too.
-// K2: GEMM + epilogue.
-// hs: single-Hadamard weight planes (requires sym).
+// K2 for single-Hadamard weight planes (requires sym).
 hipError_t launch_gemm(const GemmArgs& g, int a4, int sym, int cfg, int hs, hipStream_t s);
+// K2 for every other plan (k_gemm1.hip, one object per activation width and
+// scale mode). w4: 4-bit weights packed two per byte.
+hipError_t launch_gemm1_a0_s0(const GemmArgs& g, int cfg, int w4, hipStream_t s);
+hipError_t launch_gemm1_a0_s1(const GemmArgs& g, int cfg, int w4, hipStream_t s);
+hipError_t launch_gemm1_a1_s0(const GemmArgs& g, int cfg, int w4, hipStream_t s);
+hipError_t launch_gemm1_a1_s1(const GemmArgs& g, int cfg, int w4, hipStream_t s);
+inline hipError_t launch_gemm1(const GemmArgs& g, int a4, int sym, int cfg, int w4,
+                               hipStream_t s) {
+  if (a4) return sym ? launch_gemm1_a1_s1(g, cfg, w4, s) : launch_gemm1_a1_s0(g, cfg, w4, s);
+  return sym ? launch_gemm1_a0_s1(g, cfg, w4, s) : launch_gemm1_a0_s0(g, cfg, w4, s);
+}
 
 // K3: standalone CFG combine.
 hipError_t launch_cfg_combine(const float* Y, int64_t half_elems, float w, float* out,
@@ -87,6 +100,11 @@ hipError_t launch_quantize_weights(const float* W, const float* sw, int N, int K
 // caller). K % 4 == 0 and K % hadamard_block == 0.
 hipError_t launch_fwht_split(const uint8_t* codes, int N, int K, int hadamard_block, uint8_t* out,
                              hipStream_t s);
+// 4-bit codes (int8 in [-8, 7], n % 16 == 0, 16-byte aligned) packed two
+// per byte: element 2i in the low nibble of byte i.
+hipError_t launch_pack4(const uint8_t* codes, int64_t n, uint8_t* packed, hipStream_t s);
+// Packed 4-bit codes back to int8, the k (0..3) low magnitude bits cleared.
+hipError_t launch_unpack4(const uint8_t* packed, int64_t n, int k, uint8_t* codes, hipStream_t s);
 // Weight codes with the k low magnitude bits cleared (nbytes % 16 == 0,
 // 16-byte aligned), and a copy of the nsw weight scales.
 hipError_t launch_truncate_weights(const uint8_t* in, int64_t nbytes, int k, uint8_t* out,

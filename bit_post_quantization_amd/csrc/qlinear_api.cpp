@@ -7,11 +7,25 @@
 
 #include <cstdarg>
 #include <cstdio>
+#include <memory>
 #include <mutex>
 #include <string>
 #include <vector>
 
 #include "ql_kernels.h"
+
+namespace {
+// Device buffer shared by a plan and its TASQ views (freed with the last).
+using DevBuf = std::shared_ptr<uint8_t>;
+
+hipError_t dev_alloc(DevBuf& out, size_t bytes) {
+  void* p = nullptr;
+  const hipError_t e = hipMalloc(&p, bytes);
+  if (e != hipSuccess) return e;
+  out = DevBuf(static_cast<uint8_t*>(p), [](uint8_t* q) { (void)hipFree(q); });
+  return hipSuccess;
+}
+}  // namespace
 
 struct qlinear_plan {
   ql_desc d;
@@ -19,11 +33,18 @@ struct qlinear_plan {
   std::vector<int32_t> kseg; // input branch offsets, nks + 1 ({0, K} without branches)
   int nks = 1;
   int device = -1;
-  uint8_t* wq = nullptr;     // GEMM weights: codes int8 [N,K], or the two planes of
-                             // H W_int^T, int8 [2 * roundup(N,16), K] (single Hadamard)
-  uint8_t* wint = nullptr;   // single Hadamard: the codes W_int, int8 [N,K]
-  float* ypart = nullptr;    // input branches: the GEMM's partial-sum workspace
-  float* sw = nullptr;       // weight scales [nks, N]
+  // The GEMM (k_gemm1.hip) reads the stored codes and applies the TASQ
+  // depth itself: every plan but the single-Hadamard one and those with 3
+  // or 4 input branches. Views of such plans share the weights.
+  bool depth_in_gemm = false;
+  bool packed4 = false;      // 4-bit codes stored two per byte (depth_in_gemm plans)
+  int w_lsb_k = 0;           // TASQ depth the GEMM applies (views of depth_in_gemm plans)
+  DevBuf wq;                 // GEMM weights: codes int8 [N,K], packed 4-bit [N,K/2], or
+                             // the two planes of H W_int^T, int8 [2 * roundup(N,16), K]
+                             // (single Hadamard)
+  DevBuf wint;               // single Hadamard: the codes W_int, int8 [N,K]
+  DevBuf sw;                 // weight scales [nks, N] (float)
+  float* ypart = nullptr;    // 3-4 input branches: the GEMM's partial-sum workspace
   ql::ReduceWs* ws = nullptr;
 };
 
@@ -119,10 +140,10 @@ ql_status check_desc(const ql_desc* d) {
   return QL_OK;
 }
 
-// Partial-sum workspace of the GEMM for plans with input branches (one
-// block per compute unit of the device).
+// Partial-sum workspace of the single-Hadamard / many-branch GEMM for plans
+// with 3 or 4 input branches (one block per compute unit of the device).
 hipError_t alloc_ypart(struct qlinear_plan* p) {
-  if (p->nks <= 1) return hipSuccess;
+  if (p->depth_in_gemm || p->nks <= 1) return hipSuccess;
   int cus = 0;
   hipError_t e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, p->device);
   if (e != hipSuccess) return e;
@@ -146,9 +167,6 @@ ql_status check_plan(qlinear_plan_t p) {
 
 void free_plan(struct qlinear_plan* p) {
   if (!p) return;
-  if (p->wq) (void)hipFree(p->wq);
-  if (p->sw) (void)hipFree(p->sw);
-  if (p->wint) (void)hipFree(p->wint);
   if (p->ypart) (void)hipFree(p->ypart);
   if (p->ws) (void)hipFree(p->ws);
   delete p;
@@ -165,19 +183,22 @@ bool same_layer(const struct qlinear_plan* a, const struct qlinear_plan* b) {
          a->kseg == b->kseg && a->device == b->device;
 }
 
-// Enqueue view's weights = base's codes with k low magnitude bits cleared,
-// and base's scales.
+// Plans whose GEMM does not apply the depth (single Hadamard: the planes
+// are built from the truncated codes; 3-4 input branches): enqueue view's
+// weights = base's codes with k low magnitude bits cleared, and base's
+// scales.
 ql_status enqueue_lsb(struct qlinear_plan* view, const struct qlinear_plan* base, int k,
                       hipStream_t s) {
   const int64_t nbytes = (int64_t)base->d.N * base->d.K;
   const bool single = base->d.single_hadamard != 0;
-  hipError_t e = ql::launch_truncate_weights(single ? base->wint : base->wq, nbytes, k,
-                                             single ? view->wint : view->wq, base->sw, view->sw,
-                                             base->nks * base->d.N, s);
+  hipError_t e = ql::launch_truncate_weights(
+      single ? base->wint.get() : base->wq.get(), nbytes, k,
+      single ? view->wint.get() : view->wq.get(), reinterpret_cast<const float*>(base->sw.get()),
+      reinterpret_cast<float*>(view->sw.get()), base->nks * base->d.N, s);
   if (e != hipSuccess) return hip_fail(e, "truncating weight codes");
   if (single) {  // rebuild the hi/lo planes from the truncated codes
-    e = ql::launch_fwht_split(view->wint, base->d.N, base->d.K, base->d.hadamard_block, view->wq,
-                              s);
+    e = ql::launch_fwht_split(view->wint.get(), base->d.N, base->d.K, base->d.hadamard_block,
+                              view->wq.get(), s);
     if (e != hipSuccess) return hip_fail(e, "single-Hadamard weight planes");
   }
   return QL_OK;
@@ -293,19 +314,23 @@ ql_status qlinear_plan(const ql_desc* d, const float* W, void* stream, qlinear_p
     return fail(QL_ERR_HIP, "hipGetDevice failed");
   }
   const int64_t N = d->N, K = d->K;
-  // Weight codes are stored one per byte for both widths (4-bit codes lie
-  // in [-7, 7]); the GEMM reads them without an unpack step.
+  // 4-bit codes are stored two per byte [N, K/2] where the GEMM unpacks
+  // them (depth_in_gemm plans), one per byte otherwise.
   const bool single = d->single_hadamard != 0;
+  p->depth_in_gemm = !single && p->nks <= 2;
+  p->packed4 = p->depth_in_gemm && d->w_bits == 4;
   const size_t wbytes = (size_t)(N * K);
-  const size_t gbytes = single ? gemm_weight_rows(*d) * (size_t)K : wbytes;
+  const size_t gbytes = single ? gemm_weight_rows(*d) * (size_t)K : p->packed4 ? wbytes / 2 : wbytes;
   float* rot = nullptr;
   uint32_t* rowmax = nullptr;
   int32_t* segd = nullptr;
+  uint8_t* codes8 = nullptr;  // packed plans: the codes one per byte, before packing
   hipError_t e = hipSuccess;
   auto cleanup = [&]() {
     if (rot) (void)hipFree(rot);
     if (rowmax) (void)hipFree(rowmax);
     if (segd) (void)hipFree(segd);
+    if (codes8) (void)hipFree(codes8);
   };
   // On failure, let the work already enqueued finish before its buffers go.
 #define QL_TRY(expr, what)                \
@@ -318,9 +343,10 @@ ql_status qlinear_plan(const ql_desc* d, const float* W, void* stream, qlinear_p
       return hip_fail(e, what);           \
     }                                     \
   } while (0)
-  QL_TRY(hipMalloc(&p->wq, gbytes), "allocating weight codes");
-  if (single) QL_TRY(hipMalloc(&p->wint, wbytes), "allocating unrotated weight codes");
-  QL_TRY(hipMalloc(&p->sw, (size_t)p->nks * N * sizeof(float)), "allocating weight scales");
+  QL_TRY(dev_alloc(p->wq, gbytes), "allocating weight codes");
+  if (single) QL_TRY(dev_alloc(p->wint, wbytes), "allocating unrotated weight codes");
+  if (p->packed4) QL_TRY(hipMalloc(&codes8, wbytes), "allocating unpacked weight codes");
+  QL_TRY(dev_alloc(p->sw, (size_t)p->nks * N * sizeof(float)), "allocating weight scales");
   QL_TRY(hipMalloc(&p->ws, sizeof(ql::ReduceWs)), "allocating reduction workspace");
   QL_TRY(hipMalloc(&rowmax, N * sizeof(uint32_t)), "allocating row maxima");
   QL_TRY(alloc_ypart(p), "allocating partial-sum workspace");
@@ -347,19 +373,20 @@ ql_status qlinear_plan(const ql_desc* d, const float* W, void* stream, qlinear_p
   const float qw = (float)qmax(d->w_bits);
   // Every input branch (the whole row without branches) has its own scales
   // over its own columns.
+  uint8_t* codes_out = single ? p->wint.get() : p->packed4 ? codes8 : p->wq.get();
   for (int j = 0; j < p->nks; ++j) {
     const int c0 = p->kseg[j], cw = p->kseg[j + 1] - p->kseg[j];
-    float* swj = p->sw + (int64_t)j * N;
+    float* swj = reinterpret_cast<float*>(p->sw.get()) + (int64_t)j * N;
     QL_TRY(ql::launch_row_absmax(src, (int)N, (int)K, c0, cw, rowmax, s), "weight row maxima");
     QL_TRY(ql::launch_weight_scales(rowmax, (int)N, mode, segd, ngroups, qw, swj, s),
            "weight scales");
-    QL_TRY(ql::launch_quantize_weights(src, swj, (int)N, (int)K, c0, cw, qw,
-                                       single ? p->wint : p->wq, s),
+    QL_TRY(ql::launch_quantize_weights(src, swj, (int)N, (int)K, c0, cw, qw, codes_out, s),
            "weight codes");
   }
+  if (p->packed4) QL_TRY(ql::launch_pack4(codes8, N * K, p->wq.get(), s), "packing weight codes");
   if (single) {
-    QL_TRY(hipMemsetAsync(p->wq, 0, gbytes, s), "clearing weight planes");
-    QL_TRY(ql::launch_fwht_split(p->wint, (int)N, (int)K, d->hadamard_block, p->wq, s),
+    QL_TRY(hipMemsetAsync(p->wq.get(), 0, gbytes, s), "clearing weight planes");
+    QL_TRY(ql::launch_fwht_split(p->wint.get(), (int)N, (int)K, d->hadamard_block, p->wq.get(), s),
            "single-Hadamard weight planes");
   }
   QL_TRY(hipStreamSynchronize(s), "synchronising plan stream");
@@ -388,16 +415,33 @@ ql_status qlinear_plan_lsb_view(qlinear_plan_t base, int32_t w_lsb_k, void* stre
   v->kseg = base->kseg;
   v->nks = base->nks;
   v->device = base->device;
+  v->depth_in_gemm = base->depth_in_gemm;
+  v->packed4 = base->packed4;
+  if (base->depth_in_gemm) {
+    // TASQ's one stored buffer: the view shares the base's codes and scales
+    // and carries the depth, which the GEMM applies as it loads the codes
+    // (clearing k bits after k' cleared clears max(k, k')).
+    v->wq = base->wq;
+    v->sw = base->sw;
+    v->w_lsb_k = w_lsb_k > base->w_lsb_k ? w_lsb_k : base->w_lsb_k;
+    const hipError_t e = hipMalloc(&v->ws, sizeof(ql::ReduceWs));
+    if (e != hipSuccess) {
+      free_plan(v);
+      return hip_fail(e, "allocating view plan");
+    }
+    *out = v;
+    return ok();
+  }
   const size_t wbytes = (size_t)base->d.N * base->d.K;
   const size_t gbytes = gemm_weight_rows(base->d) * (size_t)base->d.K;
-  hipError_t e = hipMalloc(&v->wq, gbytes);
-  if (e == hipSuccess) e = hipMalloc(&v->sw, (size_t)base->nks * base->d.N * sizeof(float));
+  hipError_t e = dev_alloc(v->wq, gbytes);
+  if (e == hipSuccess) e = dev_alloc(v->sw, (size_t)base->nks * base->d.N * sizeof(float));
   if (e == hipSuccess) e = hipMalloc(&v->ws, sizeof(ql::ReduceWs));
   if (e == hipSuccess) e = alloc_ypart(v);
   if (e == hipSuccess && base->d.single_hadamard) {
-    e = hipMalloc(&v->wint, wbytes);
+    e = dev_alloc(v->wint, wbytes);
     // rows past N of the planes stay zero for the life of the view
-    if (e == hipSuccess) e = hipMemsetAsync(v->wq, 0, gbytes, s);
+    if (e == hipSuccess) e = hipMemsetAsync(v->wq.get(), 0, gbytes, s);
   }
   if (e != hipSuccess) {
     free_plan(v);
@@ -429,6 +473,12 @@ ql_status qlinear_plan_lsb_update(qlinear_plan_t view, qlinear_plan_t base, int3
     return fail(QL_ERR_ARG, "view and base differ in descriptor or segments");
   if (w_lsb_k < 0 || w_lsb_k >= base->d.w_bits)
     return fail(QL_ERR_ARG, "w_lsb_k = %d must be in [0, %d)", w_lsb_k, base->d.w_bits);
+  if (view->depth_in_gemm) {  // a new depth over the base's buffer, no data moved
+    view->wq = base->wq;
+    view->sw = base->sw;
+    view->w_lsb_k = w_lsb_k > base->w_lsb_k ? w_lsb_k : base->w_lsb_k;
+    return ok();
+  }
   st = enqueue_lsb(view, base, w_lsb_k, reinterpret_cast<hipStream_t>(stream));
   if (st != QL_OK) return st;
   return ok();
@@ -440,12 +490,21 @@ ql_status qlinear_plan_weights(qlinear_plan_t p, int8_t* w_codes, float* w_scale
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   hipError_t e;
   if (w_codes) {
-    e = hipMemcpyAsync(w_codes, p->d.single_hadamard ? p->wint : p->wq, (size_t)p->d.N * p->d.K,
-                       hipMemcpyDeviceToDevice, s);
+    const int64_t n = (int64_t)p->d.N * p->d.K;
+    uint8_t* out = reinterpret_cast<uint8_t*>(w_codes);
+    if (p->packed4) {
+      e = ql::launch_unpack4(p->wq.get(), n, p->w_lsb_k, out, s);
+    } else if (p->w_lsb_k > 0) {
+      if (!aligned(w_codes, 16)) return fail(QL_ERR_ARG, "w_codes must be 16-byte aligned");
+      e = ql::launch_truncate_weights(p->wq.get(), n, p->w_lsb_k, out, nullptr, nullptr, 0, s);
+    } else {
+      e = hipMemcpyAsync(w_codes, p->d.single_hadamard ? p->wint.get() : p->wq.get(), (size_t)n,
+                         hipMemcpyDeviceToDevice, s);
+    }
     if (e != hipSuccess) return hip_fail(e, "copying weight codes");
   }
   if (w_scales) {
-    e = hipMemcpyAsync(w_scales, p->sw, (size_t)p->nks * p->d.N * sizeof(float),
+    e = hipMemcpyAsync(w_scales, p->sw.get(), (size_t)p->nks * p->d.N * sizeof(float),
                        hipMemcpyDeviceToDevice, s);
     if (e != hipSuccess) return hip_fail(e, "copying weight scales");
   }
@@ -492,9 +551,9 @@ ql_status qlinear_gemm(qlinear_plan_t p, const void* codes, const float* act_sca
     return fail(QL_ERR_ARG, "Y, act_scales and acc_dbg must be 4-byte aligned");
   ql::GemmArgs g;
   g.A = reinterpret_cast<const uint8_t*>(codes);
-  g.W = p->wq;
+  g.W = p->wq.get();
   g.act_scales = act_scales;
-  g.w_scales = p->sw;
+  g.w_scales = reinterpret_cast<const float*>(p->sw.get());
   g.Y = Y;
   g.dbg = acc_dbg;
   g.M = M;
@@ -503,19 +562,29 @@ ql_status qlinear_gemm(qlinear_plan_t p, const void* codes, const float* act_sca
   g.K = p->d.K;
   g.Mh = cfg ? M / 2 : M;
   g.lda = p->d.a_bits == 4 ? p->d.K / 2 : p->d.K;
-  g.ldw = p->d.K;
+  g.ldw = p->packed4 ? p->d.K / 2 : p->d.K;
   if ((int64_t)M * g.lda >= ((int64_t)1 << 31) || (int64_t)g.N * g.ldw >= ((int64_t)1 << 31))
     return fail(QL_ERR_UNSUPPORTED, "codes or weights of 2 GiB or more (M = %d)", M);
+  // Output offsets within a 128-row tile are 32-bit byte offsets.
+  if ((int64_t)g.N * 4 * 128 >= ((int64_t)1 << 31))
+    return fail(QL_ERR_UNSUPPORTED, "N = %d: a 128-row block of Y reaches 2 GiB", g.N);
   g.guidance = w;
   g.inv_b = p->d.hadamard_block ? 1.0f / (float)p->d.hadamard_block : 1.0f;
   g.nks = p->nks;
   g.ypart_ws = p->ypart;
   for (int j = 0; j < ql::kMaxKSeg; ++j)
     g.ks_end[j] = j + 1 < p->nks ? p->kseg[j + 1] / 128 : 0x7FFFFFFF;
-  hipError_t e = ql::launch_gemm(g, p->d.a_bits == 4,
-                                 p->d.a_scale_mode == QL_ASCALE_SYMMETRIC, cfg,
-                                 p->d.single_hadamard,
-                                 reinterpret_cast<hipStream_t>(stream));
+  for (int j = 0; j <= ql::kMaxKSeg; ++j) g.kofs[j] = j < p->nks ? p->kseg[j] : p->d.K;
+  for (int j = 0; j < ql::kMaxKSeg; ++j) {
+    const int steps = j < p->nks ? (p->kseg[j + 1] - p->kseg[j] + 127) / 128 : 0;
+    g.ksteps[j] = (steps + 2) / 3 * 3;
+  }
+  g.w_lsb_k = p->w_lsb_k;
+  const int a4 = p->d.a_bits == 4, sym = p->d.a_scale_mode == QL_ASCALE_SYMMETRIC;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  const hipError_t e = p->depth_in_gemm
+                           ? ql::launch_gemm1(g, a4, sym, cfg, p->packed4, s)
+                           : ql::launch_gemm(g, a4, sym, cfg, p->d.single_hadamard, s);
   if (e != hipSuccess) return hip_fail(e, "launching gemm");
   return ok();
 }

@@ -114,10 +114,11 @@ typedef struct {
  * (s = absmax / qmax_w, qmax_w = 2^(w_bits-1) - 1), quantize
  * (round half to even, clamp to [-qmax_w, qmax_w]); with input branches,
  * each branch's columns get their own scales, s_w[j][n], by the same rule
- * over those columns only. The plan keeps one
- * signed byte per weight code for both widths (4-bit codes lie in [-7, 7]):
- * the GEMM is bound by its matrix-core and vector issue, not by weight bytes,
- * so it reads 4-bit weights without an unpack step.
+ * over those columns only. Storage: 4-bit codes (in [-7, 7]) are kept two
+ * per byte, [N, K/2], code 2i in the low nibble of byte i (the layout of
+ * the 4-bit activation codes), and unpacked by the GEMM in LDS; 8-bit codes
+ * one per byte. Exceptions, one byte per code: single_hadamard plans and
+ * plans with 3 or 4 input branches.
  *   d   : HOST descriptor (copied; seg_offsets and k_seg_offsets copied too).
  *   W   : DEVICE fp32 [N,K]; read only, may be freed after the call.
  *   out : HOST; receives the plan handle.
@@ -126,6 +127,8 @@ typedef struct {
  * descriptor or NULL pointer, QL_ERR_UNSUPPORTED for more than 4 input
  * branches, an inner branch offset that is not a multiple of 128, or input
  * branches with single_hadamard, QL_ERR_OOM, QL_ERR_HIP.
+ * Method: DualScale weight side -- SegQuant explainer 2.B; per-segment
+ * scales -- SegQuant explainer 2.A; rotation -- HQ-DM explainer 2.1.
  */
 ql_status qlinear_plan(const ql_desc* d, const float* W, void* stream, qlinear_plan_t* out);
 /* With single_hadamard = 1 the plan quantizes W without rotation (scales and
@@ -140,9 +143,10 @@ ql_status qlinear_plan(const ql_desc* d, const float* W, void* stream, qlinear_p
 ql_status qlinear_plan_destroy(qlinear_plan_t p);
 
 /* Copy a plan's weights out for inspection: w_codes DEVICE int8 [N,K]
- * (one code per byte; the unrotated W_int for single_hadamard), w_scales
- * DEVICE fp32 [S,N] (S input branches, 1 without). Either may be NULL to
- * skip it. */
+ * (one code per byte, unpacked if stored packed; a view's codes with its
+ * depth applied; the unrotated W_int for single_hadamard; 16-byte aligned
+ * for a view), w_scales DEVICE fp32 [S,N] (S input branches, 1 without).
+ * Either may be NULL to skip it. */
 ql_status qlinear_plan_weights(qlinear_plan_t p, int8_t* w_codes, float* w_scales, void* stream);
 
 /*
@@ -155,10 +159,16 @@ ql_status qlinear_plan_weights(qlinear_plan_t p, int8_t* w_codes, float* w_scale
  *
  * qlinear_plan_lsb_view: make a new plan whose weight codes are base's
  * truncated by w_lsb_k and whose descriptor, segments and scales are base's.
- * The view owns its memory (codes, a copy of the scales, its own reduction
- * workspace), is destroyed with qlinear_plan_destroy in any order relative
- * to base, and is used in every call like a plan. Allocates device memory
- * and synchronises `stream` before it returns.
+ * As on the page, there is one stored buffer: the view shares base's codes
+ * and scales and carries the depth, which qlinear_gemm applies to the codes
+ * as it loads them (a view of a view clears max of the two depths). The
+ * view holds its own reduction workspace, is destroyed with
+ * qlinear_plan_destroy in any order relative to base (the shared buffer
+ * goes with the last of them), and is used in every call like a plan.
+ * Exceptions: views of single_hadamard plans (whose GEMM planes are built
+ * from the truncated codes) and of plans with 3 or 4 input branches hold a
+ * truncated copy of the codes and scales. Allocates device memory and
+ * synchronises `stream` before it returns.
  *   base     : plan on the current device.
  *   w_lsb_k  : 0 <= w_lsb_k < w_bits (0 gives a copy of base).
  *   out      : HOST; receives the view handle.
@@ -169,13 +179,16 @@ ql_status qlinear_plan_lsb_view(qlinear_plan_t base, int32_t w_lsb_k, void* stre
                                 qlinear_plan_t* out);
 
 /*
- * Rewrite the weights of an existing view for a new step: view's codes =
- * base's truncated by w_lsb_k, view's scales = base's. Enqueued on `stream`
- * with no allocation and no host synchronisation, so a sampler keeps one
- * operating copy per layer and changes its precision between steps. Work
- * already enqueued on view must be ordered before this call (same stream
- * or events). Errors: QL_ERR_ARG (NULL, view == base, w_lsb_k out of range,
- * view and base with different descriptors or segments), QL_ERR_HIP.
+ * Set the depth of an existing view for a new step: view's codes = base's
+ * truncated by w_lsb_k, view's scales = base's (TASQ explainer, technical
+ * summary 2). For a view sharing base's buffer this moves no data: calls
+ * made on the view after this returns use the new depth, calls enqueued
+ * before keep theirs. For a view with its own copy (see
+ * qlinear_plan_lsb_view) the rewrite is enqueued on `stream` with no
+ * allocation and no host synchronisation, and work already enqueued on the
+ * view must be ordered before this call (same stream or events). Errors:
+ * QL_ERR_ARG (NULL, view == base, w_lsb_k out of range, view and base with
+ * different descriptors or segments), QL_ERR_HIP.
  */
 ql_status qlinear_plan_lsb_update(qlinear_plan_t view, qlinear_plan_t base, int32_t w_lsb_k,
                                   void* stream);
