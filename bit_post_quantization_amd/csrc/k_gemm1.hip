@@ -134,12 +134,16 @@ __device__ __forceinline__ v4i positive(v4i c) {
 // magnitude cleared, sign kept, i.e. rounding toward zero to a multiple of
 // 2^kk. A negative byte gets 2^kk - 1 added before its low bits are
 // cleared; the add runs on the low 7 bits (at most 127 + 127, so no carry
-// leaves a byte) and the sign bit is put back by exclusive or.
-// sh = 7 - kk; keep = the byte ~(2^kk - 1) in every byte.
-__device__ __forceinline__ uint32_t trunc_mag4(uint32_t b, int sh, uint32_t keep) {
+// leaves a byte) and the sign bit is put back by exclusive or. The bias
+// comes from a byte table: v_perm_b32 with selector 0 or 1 per byte (the
+// byte's sign bit) picks byte 0 (= 0) or byte 1 (= 2^kk - 1) of lut. Five
+// VALU instructions.
+// lut = (2^kk - 1) << 8; keep = the byte ~(2^kk - 1) in every byte.
+__device__ __forceinline__ uint32_t trunc_mag4(uint32_t b, uint32_t lut, uint32_t keep) {
   const uint32_t h = b & 0x80808080u;
-  const uint32_t bias = (h >> sh) - (h >> 7);
-  const uint32_t s = (b ^ h) + bias;
+  const uint32_t bias = __builtin_amdgcn_perm(0u, lut, h >> 7);
+  uint32_t s;
+  asm("v_xad_u32 %0, %1, %2, %3" : "=v"(s) : "v"(b), "v"(h), "v"(bias));  // (b ^ h) + bias
   return (s ^ h) & keep;
 }
 
@@ -201,9 +205,10 @@ __device__ __forceinline__ TileList my_tiles(int T, int ct) {
 }
 
 // Weight formats of the ring.
-constexpr int kWInt8 = 0;     // int8 codes, used as loaded
-constexpr int kWPacked4 = 1;  // 4-bit codes two per byte, unpacked x16 in LDS (TASQ mask optional)
-constexpr int kWMasked8 = 2;  // int8 codes, TASQ mask applied in LDS
+constexpr int kWInt8 = 0;          // int8 codes, used as loaded
+constexpr int kWPacked4 = 1;       // 4-bit codes two per byte, unpacked x16 in LDS
+constexpr int kWMasked8 = 2;       // int8 codes, TASQ mask applied in LDS
+constexpr int kWPacked4Masked = 3; // 4-bit codes, unpacked and masked in LDS
 
 // Bytes of one ring slot: the activation fragment pairs of the 4 waves, the
 // NB int8 weight fragment images, and (packed 4-bit weights) the NB packed
@@ -213,7 +218,7 @@ struct Slot {
   static constexpr int kAFrag = A4 ? 1024 : 2048;  // one activation fragment pair
   static constexpr int kA = 4 * 2 * kAFrag;        // 4 waves x 2 fragments
   static constexpr int kW = NB * 2048;
-  static constexpr int kStage = WX == kWPacked4 ? NB * 1024 : 0;
+  static constexpr int kStage = (WX == kWPacked4 || WX == kWPacked4Masked) ? NB * 1024 : 0;
   static constexpr int kBytes = kA + kW + kStage;
 };
 
@@ -224,21 +229,23 @@ struct ScaleRing {
   static constexpr int kFloats = 4 * kBranches * 256;
 };
 
-// The work of one wave. TW: this wave also moves weight fragment w + 8.
-template <bool A4, bool SYM, bool CFG, int WX, bool KS, int NB, bool TW>
+// The work of one wave. Wave w moves weight fragments w and w + 4; XW: it
+// also moves (a DMA instruction of) fragment 8, which waves 0 and 1 share
+// for int8 weights (one instruction each) and wave 0 moves for packed ones.
+template <bool A4, bool SYM, bool CFG, int WX, bool KS, int NB, bool XW>
 __device__ __forceinline__ void gemm_wave(const GemmArgs& g, int wave, int lane, uint8_t* st0,
                                           uint8_t* st1, uint8_t* st2, float* sring) {
   using SL = Slot<A4, WX, NB>;
-  constexpr bool W4 = WX == kWPacked4;
+  constexpr bool W4 = WX == kWPacked4 || WX == kWPacked4Masked;
+  constexpr bool MASK = WX == kWMasked8 || WX == kWPacked4Masked;
   constexpr int NP = SYM ? 1 : 2;                    // accumulator planes
   constexpr int SHIFT = (A4 ? 4 : 0) + (W4 ? 4 : 0);  // undo the x16 unpacks
   constexpr int BN = 16 * NB;
   constexpr int RPT = CFG ? 64 : 128;    // output rows per tile
   constexpr int kALoads = A4 ? 1 : 2;    // DMA instructions per activation fragment pair
-  constexpr int kWFrags = TW ? 3 : 2;    // weight fragments this wave moves
   constexpr int kWLoads = W4 ? 1 : 2;    // DMA instructions per weight fragment
   constexpr int kOpsA = 2 * kALoads;
-  constexpr int kOpsW = kWFrags * kWLoads;
+  constexpr int kOpsW = 2 * kWLoads + (XW ? 1 : 0);
   constexpr int kOps = kOpsA + kOpsW;    // vector-memory instructions per step and wave
   constexpr int kSR = ScaleRing<KS>::kBranches;
   static_assert(NB >= 8 && NB <= 9, "weight fragments per tile");
@@ -295,7 +302,14 @@ __device__ __forceinline__ void gemm_wave(const GemmArgs& g, int wave, int lane,
   // and epilogue read them there. Entry ti % 4 is refilled for tile ti + 4
   // at least one step after the epilogue of tile ti.
   int w_ti = 0, w_j = 0, w_k = 0, a_ti = 0, a_j = 0, a_k = 0;
-  unsigned wv[3][2], av[2][2];
+  unsigned wv[kOpsW], av[2][2];
+  // Weight DMA instruction o of this wave: fragment and instruction index.
+  auto w_frag = [&](int o) __attribute__((always_inline)) {
+    return o < 2 * kWLoads ? wave + 4 * (o / kWLoads) : 8;
+  };
+  auto w_inst = [&](int o) __attribute__((always_inline)) {
+    return o < 2 * kWLoads ? o % kWLoads : (W4 ? 0 : wave);
+  };
   auto w_enter = [&](int ti) __attribute__((always_inline)) {
     int m0, n0;
     coords(ti, m0, n0);
@@ -307,19 +321,17 @@ __device__ __forceinline__ void gemm_wave(const GemmArgs& g, int wave, int lane,
             4u * (unsigned)(j * g.N + n0), 0, 0);
     }
 #pragma unroll
-    for (int q = 0; q < kWFrags; ++q)
-#pragma unroll
-      for (int i = 0; i < kWLoads; ++i) {
-        if constexpr (W4) {
-          const int n = n0 + 16 * (wave + 4 * q) + (lane >> 2);
-          wv[q][i] = n < g.N ? (unsigned)n * (unsigned)g.ldw + 16u * (unsigned)(lane & 3) : kOOB;
-        } else {
-          const int n = n0 + 16 * (wave + 4 * q) + WFrag::dma_row(i, lane);
-          wv[q][i] = n < g.N ? (unsigned)n * (unsigned)g.ldw +
-                                   16u * (unsigned)WFrag::dma_chunk(i, lane)
-                             : kOOB;
-        }
+    for (int o = 0; o < kOpsW; ++o) {
+      const int f = w_frag(o), i = w_inst(o);
+      if constexpr (W4) {
+        const int n = n0 + 16 * f + (lane >> 2);
+        wv[o] = n < g.N ? (unsigned)n * (unsigned)g.ldw + 16u * (unsigned)(lane & 3) : kOOB;
+      } else {
+        const int n = n0 + 16 * f + WFrag::dma_row(i, lane);
+        wv[o] = n < g.N ? (unsigned)n * (unsigned)g.ldw + 16u * (unsigned)WFrag::dma_chunk(i, lane)
+                        : kOOB;
       }
+    }
   };
   auto a_enter = [&](int ti) __attribute__((always_inline)) {
     int m0, n0;
@@ -336,22 +348,26 @@ __device__ __forceinline__ void gemm_wave(const GemmArgs& g, int wave, int lane,
       }
   };
   // One DMA instruction of each stream's current step (chunks past the end
-  // of the branch read zeros): weight fragment wave + 4q, instruction i;
+  // of the branch read zeros): weight instruction o of this wave;
   // activation fragment fi of this wave, instruction i.
-  auto w_op = [&](uint8_t* slot, int q, int i) __attribute__((always_inline)) {
+  auto w_dst = [&](uint8_t* slot, int o) __attribute__((always_inline)) {
+    if constexpr (W4)
+      return slot + SL::kA + SL::kW + w_frag(o) * 1024;
+    else
+      return slot + SL::kA + w_frag(o) * 2048 + w_inst(o) * 1024;
+  };
+  auto w_op = [&](uint8_t* slot, int o) __attribute__((always_inline)) {
     const int k0 = kbeg(w_j) + w_k * BK;
     const int ke = kend(w_j);
-    unsigned v = wv[q][i];
+    unsigned v = wv[o];
     if constexpr (W4) {
       if (k0 + BK > ke && k0 + 32 * (lane & 3) >= ke) v = kOOB;
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          rw, (lds_void*)(slot + SL::kA + SL::kW + (wave + 4 * q) * 1024), 16, v,
-          (unsigned)k0 / 2u, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rw, (lds_void*)w_dst(slot, o), 16, v,
+                                               (unsigned)k0 / 2u, 0, 0);
     } else {
-      if (k0 + BK > ke && k0 + 16 * WFrag::dma_chunk(i, lane) >= ke) v = kOOB;
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          rw, (lds_void*)(slot + SL::kA + (wave + 4 * q) * 2048 + i * 1024), 16, v,
-          (unsigned)k0, 0, 0);
+      if (k0 + BK > ke && k0 + 16 * WFrag::dma_chunk(w_inst(o), lane) >= ke) v = kOOB;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rw, (lds_void*)w_dst(slot, o), 16, v,
+                                               (unsigned)k0, 0, 0);
     }
   };
   auto a_op = [&](uint8_t* slot, int fi, int i) __attribute__((always_inline)) {
@@ -373,9 +389,7 @@ __device__ __forceinline__ void gemm_wave(const GemmArgs& g, int wave, int lane,
       w_enter(w_ti);
     } else {
 #pragma unroll
-      for (int q = 0; q < kWFrags; ++q)
-#pragma unroll
-        for (int i = 0; i < kWLoads; ++i) wv[q][i] = kOOB;
+      for (int o = 0; o < kOpsW; ++o) wv[o] = kOOB;
     }
   };
   auto a_advance = [&]() __attribute__((always_inline)) {
@@ -398,13 +412,13 @@ __device__ __forceinline__ void gemm_wave(const GemmArgs& g, int wave, int lane,
     constexpr int kMin = kOpsW < kOpsA ? kOpsW : kOpsA;
     if (o < 2 * kMin) {
       if (o % 2 == 0)
-        w_op(slot, (o / 2) / kWLoads, (o / 2) % kWLoads);
+        w_op(slot, o / 2);
       else
         a_op(slot, (o / 2) / kALoads, (o / 2) % kALoads);
     } else {
       const int k = kMin + (o - 2 * kMin);
       if (kOpsW > kOpsA)
-        w_op(slot, k / kWLoads, k % kWLoads);
+        w_op(slot, k);
       else
         a_op(slot, k / kALoads, k % kALoads);
     }
@@ -416,61 +430,75 @@ __device__ __forceinline__ void gemm_wave(const GemmArgs& g, int wave, int lane,
     a_advance();
   };
 
-  // ---- weight transform: unit t of this wave's loads of a step (one DMA
-  // instruction's 16 bytes per lane), read back by the lane that loaded it,
-  // transformed, and written as int8 image bytes.
+  // ---- weight transform: unit t = weight DMA instruction t of this wave
+  // (16 bytes per lane), read back by the lane that loaded it, transformed,
+  // and written as int8 image bytes.
   constexpr int kTUnits = WX == kWInt8 ? 0 : kOpsW;
-  int msh = 7;
-  uint32_t mkeep = 0xFFFFFFFFu;
-  bool mask_on = false;
-  if constexpr (WX != kWInt8) {
+  uint32_t mlut = 0, mkeep = 0xFFFFFFFFu;
+  if constexpr (MASK) {
     const int kk = g.w_lsb_k + (W4 ? 4 : 0);  // x16 codes: k + 4 low bits
-    mask_on = g.w_lsb_k > 0;
-    msh = 7 - kk;
+    mlut = ((1u << kk) - 1u) << 8;
     mkeep = 0x01010101u * (0xFFu & ~((1u << kk) - 1u));
   }
-  auto t_read = [&](const uint8_t* slot, int t) __attribute__((always_inline)) {
-    const int q = t / kWLoads, i = t % kWLoads;
-    if constexpr (W4)
-      return *reinterpret_cast<const v4u*>(slot + SL::kA + SL::kW + (wave + 4 * q) * 1024 +
-                                           lane * 16);
-    else
-      return *reinterpret_cast<const v4u*>(slot + SL::kA + (wave + 4 * q) * 2048 + i * 1024 +
-                                           lane * 16);
+  auto t_src = [&](const uint8_t* slot, int t) __attribute__((always_inline)) {
+    return (const v4u*)w_dst(const_cast<uint8_t*>(slot), t);
   };
-  auto t_write = [&](uint8_t* slot, int t, const v4u& x) __attribute__((always_inline)) {
-    const int q = t / kWLoads, i = t % kWLoads;
+  // Output dwords of input dword d of a unit: 2 (unpacked) or 1.
+  constexpr int kOutPer = W4 ? 2 : 1;
+  v4u tin[kTUnits > 0 ? kTUnits : 1];
+  uint32_t tout[kTUnits > 0 ? kTUnits : 1][4 * kOutPer];
+  auto t_dword = [&](int t, int d) __attribute__((always_inline)) {
+    const uint32_t x = tin[t][d];
+    if constexpr (W4) {
+      unpack4_x16(x, tout[t][2 * d], tout[t][2 * d + 1]);
+      if constexpr (MASK) {
+        tout[t][2 * d] = trunc_mag4(tout[t][2 * d], mlut, mkeep);
+        tout[t][2 * d + 1] = trunc_mag4(tout[t][2 * d + 1], mlut, mkeep);
+      }
+    } else {
+      tout[t][d] = trunc_mag4(x, mlut, mkeep);
+    }
+  };
+  auto t_write = [&](uint8_t* slot, int t) __attribute__((always_inline)) {
     if constexpr (W4) {
       // lane p holds elements 32 (p%4) .. +31 of row p/4: image chunks
       // 2 (p%4) and 2 (p%4) + 1 of that row
-      uint32_t o[8];
-#pragma unroll
-      for (int d = 0; d < 4; ++d) unpack4_x16(x[d], o[2 * d], o[2 * d + 1]);
-      if (mask_on) {
-#pragma unroll
-        for (int d = 0; d < 8; ++d) o[d] = trunc_mag4(o[d], msh, mkeep);
-      }
-      uint8_t* img = slot + SL::kA + (wave + 4 * q) * 2048;
+      uint8_t* img = slot + SL::kA + w_frag(t) * 2048;
       const int r = lane >> 2, c = 2 * (lane & 3);
-      *reinterpret_cast<v4u*>(img + WFrag::at(r, c)) = v4u{o[0], o[1], o[2], o[3]};
-      *reinterpret_cast<v4u*>(img + WFrag::at(r, c + 1)) = v4u{o[4], o[5], o[6], o[7]};
+      *reinterpret_cast<v4u*>(img + WFrag::at(r, c)) =
+          v4u{tout[t][0], tout[t][1], tout[t][2], tout[t][3]};
+      *reinterpret_cast<v4u*>(img + WFrag::at(r, c + 1)) =
+          v4u{tout[t][4], tout[t][5], tout[t][6], tout[t][7]};
     } else {
-      v4u y;
-#pragma unroll
-      for (int d = 0; d < 4; ++d) y[d] = trunc_mag4(x[d], msh, mkeep);
-      *reinterpret_cast<v4u*>(slot + SL::kA + (wave + 4 * q) * 2048 + i * 1024 + lane * 16) = y;
+      *reinterpret_cast<v4u*>(w_dst(slot, t) + lane * 16) =
+          v4u{tout[t][0], tout[t][1], tout[t][2], tout[t][3]};
     }
   };
-  // Spread over a half step: unit t read after weight fragment t's MFMAs,
-  // transformed and written two fragments later.
-  v4u tb[kTUnits > 0 ? kTUnits : 1];
+  // Spread over a half step: every unit read after the first weight
+  // fragment's MFMAs; its 4 input dwords transformed a few at a time
+  // after fragments 1 .. NB-1 (the VALU work interleaves with the MFMAs
+  // instead of stalling them); a unit written once its last dword is done.
   auto xform = [&](uint8_t* slot, int jj) __attribute__((always_inline)) {
     if constexpr (kTUnits > 0) {
-      if (jj < kTUnits) tb[jj] = t_read(slot, jj);
-      if (jj >= 2 && jj - 2 < kTUnits) t_write(slot, jj - 2, tb[jj - 2]);
+      constexpr int D = 4 * kTUnits;
+      if (jj == 0) {
+#pragma unroll
+        for (int t = 0; t < kTUnits; ++t) tin[t] = *(t_src(slot, t) + lane);
+      } else {
+        const int lo = D * (jj - 1) / (NB - 1), hi = D * jj / (NB - 1);
+#pragma unroll
+        for (int d = 0; d < D; ++d)
+          if (d >= lo && d < hi) {
+            t_dword(d / 4, d % 4);
+            if (d % 4 == 3) t_write(slot, d / 4);
+          }
+      }
     }
   };
-  static_assert(kTUnits + 2 <= NB, "transform units fit in a half step");
+  auto xform_all = [&](uint8_t* slot) __attribute__((always_inline)) {
+#pragma unroll
+    for (int jj = 0; jj < NB; ++jj) xform(slot, jj);
+  };
 
   // ---- operands ----
   const int rw0 = WFrag::read_off(lane, 0), rw1 = WFrag::read_off(lane, 1);
@@ -744,8 +772,7 @@ __device__ __forceinline__ void gemm_wave(const GemmArgs& g, int wave, int lane,
   issue_all(slots[2]);
   wait_vmcnt<2 * kOps>();
   if constexpr (kTUnits > 0) {
-#pragma unroll
-    for (int t = 0; t < kTUnits; ++t) t_write(slots[0], t, t_read(slots[0], t));
+    xform_all(slots[0]);
     wait_lgkm0();
   }
   __builtin_amdgcn_s_barrier();
@@ -833,8 +860,11 @@ __global__ __launch_bounds__(kThreads, 1) void k2_gemm1(GemmArgs g) {
   __shared__ __attribute__((aligned(16))) float sring[ScaleRing<KS>::kFloats];
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // uniform
-  // waves w < NB - 8 also move weight fragment w + 8
-  if (wave < NB - 8)
+  // fragment 8 (NB = 9): waves 0 and 1 one instruction each (int8 weights),
+  // wave 0 (packed weights, one instruction per fragment)
+  static_assert(NB == 9, "wave roles");
+  constexpr int kXW = (WX == kWPacked4 || WX == kWPacked4Masked) ? 1 : 2;
+  if (wave < kXW)
     gemm_wave<A4, SYM, CFG, WX, KS, NB, true>(g, wave, lane, st0, st1, st2, sring);
   else
     gemm_wave<A4, SYM, CFG, WX, KS, NB, false>(g, wave, lane, st0, st1, st2, sring);
@@ -879,7 +909,7 @@ hipError_t run_ks(const GemmArgs& g, hipStream_t s) {
 
 template <bool CFG>
 hipError_t run_wx(const GemmArgs& g, int w4, hipStream_t s) {
-  if (w4) return run_ks<CFG, kWPacked4>(g, s);
+  if (w4) return g.w_lsb_k > 0 ? run_ks<CFG, kWPacked4Masked>(g, s) : run_ks<CFG, kWPacked4>(g, s);
   if (g.w_lsb_k > 0) return run_ks<CFG, kWMasked8>(g, s);
   return run_ks<CFG, kWInt8>(g, s);
 }
