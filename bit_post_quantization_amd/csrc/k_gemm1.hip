@@ -147,6 +147,30 @@ __device__ __forceinline__ uint32_t trunc_mag4(uint32_t b, uint32_t lut, uint32_
   return (s ^ h) & keep;
 }
 
+// Nine floats at p, p + 16, ..., p + 128 (LDS), read in one asm block that
+// waits for them itself. The scale ring is written by DMA, and the compiler,
+// unable to tell which DMA wrote it, would otherwise wait for every load in
+// flight before a plain LDS read of it; the ring entry read here was written
+// tiles earlier and published by the step barriers since.
+__device__ __forceinline__ void lds_read9_stride16(const float* p, float* v) {
+  const uint32_t a = (uint32_t)reinterpret_cast<uintptr_t>(p);  // LDS offset of a shared pointer
+  asm volatile(
+      "ds_read_b32 %0, %9\n\t"
+      "ds_read_b32 %1, %9 offset:64\n\t"
+      "ds_read_b32 %2, %9 offset:128\n\t"
+      "ds_read_b32 %3, %9 offset:192\n\t"
+      "ds_read_b32 %4, %9 offset:256\n\t"
+      "ds_read_b32 %5, %9 offset:320\n\t"
+      "ds_read_b32 %6, %9 offset:384\n\t"
+      "ds_read_b32 %7, %9 offset:448\n\t"
+      "ds_read_b32 %8, %9 offset:512\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(v[0]), "=&v"(v[1]), "=&v"(v[2]), "=&v"(v[3]), "=&v"(v[4]), "=&v"(v[5]),
+        "=&v"(v[6]), "=&v"(v[7]), "=&v"(v[8])
+      : "v"(a)
+      : "memory");
+}
+
 // y from the two accumulators in the documented order, no contraction.
 template <bool SYM>
 __device__ __forceinline__ float epi_part(int accp, int accn, float sp, float sn, float sw) {
@@ -229,10 +253,13 @@ struct ScaleRing {
   static constexpr int kFloats = 4 * kBranches * 256;
 };
 
-// The work of one wave. Wave w moves weight fragments w and w + 4; XW: it
-// also moves (a DMA instruction of) fragment 8, which waves 0 and 1 share
+// The work of one wave. Wave w moves weight fragments w and w + 4; XI >= 0:
+// it also moves DMA instruction XI of fragment 8, which waves 0 and 1 share
 // for int8 weights (one instruction each) and wave 0 moves for packed ones.
-template <bool A4, bool SYM, bool CFG, int WX, bool KS, int NB, bool XW>
+// (A compile-time XI keeps every LDS address of the wave's transform
+// provably apart from the DMAs in flight; with a run-time index the compiler
+// waits for all of them.)
+template <bool A4, bool SYM, bool CFG, int WX, bool KS, int NB, int XI>
 __device__ __forceinline__ void gemm_wave(const GemmArgs& g, int wave, int lane, uint8_t* st0,
                                           uint8_t* st1, uint8_t* st2, float* sring) {
   using SL = Slot<A4, WX, NB>;
@@ -245,6 +272,7 @@ __device__ __forceinline__ void gemm_wave(const GemmArgs& g, int wave, int lane,
   constexpr int kALoads = A4 ? 1 : 2;    // DMA instructions per activation fragment pair
   constexpr int kWLoads = W4 ? 1 : 2;    // DMA instructions per weight fragment
   constexpr int kOpsA = 2 * kALoads;
+  constexpr bool XW = XI >= 0;
   constexpr int kOpsW = 2 * kWLoads + (XW ? 1 : 0);
   constexpr int kOps = kOpsA + kOpsW;    // vector-memory instructions per step and wave
   constexpr int kSR = ScaleRing<KS>::kBranches;
@@ -308,7 +336,7 @@ __device__ __forceinline__ void gemm_wave(const GemmArgs& g, int wave, int lane,
     return o < 2 * kWLoads ? wave + 4 * (o / kWLoads) : 8;
   };
   auto w_inst = [&](int o) __attribute__((always_inline)) {
-    return o < 2 * kWLoads ? o % kWLoads : (W4 ? 0 : wave);
+    return o < 2 * kWLoads ? o % kWLoads : XI;
   };
   auto w_enter = [&](int ti) __attribute__((always_inline)) {
     int m0, n0;
@@ -599,6 +627,14 @@ __device__ __forceinline__ void gemm_wave(const GemmArgs& g, int wave, int lane,
   };
 
   const int rsub = q4 * 4;
+  // Activation scales of both branches, loaded once before the load stream
+  // starts (a load here waits on every DMA in flight: vmcnt counts in order).
+  const float asc[4] = {g.act_scales[0], g.act_scales[1], KS ? g.act_scales[2] : 0.0f,
+                        KS ? g.act_scales[3] : 0.0f};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) asm volatile("" ::"v"(asc[i]));  // consumed here, not in a tile
+  auto sp_of = [&](int j) __attribute__((always_inline)) { return KS && j ? asc[2] : asc[0]; };
+  auto sn_of = [&](int j) __attribute__((always_inline)) { return KS && j ? asc[3] : asc[1]; };
 
   // Accumulator element r of slot (p, fi, jj), read out of its AGPR.
   auto acc_at = [&](int p, int fi, int jj, int r) __attribute__((always_inline)) {
@@ -628,9 +664,8 @@ __device__ __forceinline__ void gemm_wave(const GemmArgs& g, int wave, int lane,
     return epi_part<SYM>(ap, an, sp, sn, sw[jj]);
   };
   auto load_sw = [&](int ti, int j, float* sw) __attribute__((always_inline)) {
-    const float* ssl = sring + ((ti & 3) * kSR + j) * 256;
-#pragma unroll
-    for (int jj = 0; jj < NB; ++jj) sw[jj] = ssl[16 * jj + i16];
+    static_assert(NB == 9, "scale reads");
+    lds_read9_stride16(sring + ((ti & 3) * kSR + j) * 256 + i16, sw);
   };
   auto dump = [&](int m0, const unsigned* coff, int j) __attribute__((always_inline)) {
     // accumulator dump (testing aid): planes (acc+, acc-) of branch j in [2 nks, M, N]
@@ -690,7 +725,7 @@ __device__ __forceinline__ void gemm_wave(const GemmArgs& g, int wave, int lane,
     if constexpr (KS) {
       float sw[NB];
       load_sw(ti, j, sw);
-      const float spj = g.act_scales[2 * j], snj = g.act_scales[2 * j + 1];
+      const float spj = sp_of(j), snj = sn_of(j);
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
 #pragma unroll
@@ -724,7 +759,7 @@ __device__ __forceinline__ void gemm_wave(const GemmArgs& g, int wave, int lane,
     unsigned coff[NB];
     load_sw(ti, j, sw);
     col_offsets(n0, coff);
-    const float spj = g.act_scales[2 * j], snj = g.act_scales[2 * j + 1];
+    const float spj = sp_of(j), snj = sn_of(j);
     auto yout = [&](int fi, int jj, int r) __attribute__((always_inline)) {
       float y = ypart(sw, spj, snj, fi, jj, r);
       if constexpr (KS) y = __fadd_rn(ys_get((fi * NB + jj) * 4 + r), y);
@@ -864,10 +899,12 @@ __global__ __launch_bounds__(kThreads, 1) void k2_gemm1(GemmArgs g) {
   // wave 0 (packed weights, one instruction per fragment)
   static_assert(NB == 9, "wave roles");
   constexpr int kXW = (WX == kWPacked4 || WX == kWPacked4Masked) ? 1 : 2;
-  if (wave < kXW)
-    gemm_wave<A4, SYM, CFG, WX, KS, NB, true>(g, wave, lane, st0, st1, st2, sring);
+  if (wave == 0)
+    gemm_wave<A4, SYM, CFG, WX, KS, NB, 0>(g, wave, lane, st0, st1, st2, sring);
+  else if (kXW == 2 && wave == 1)
+    gemm_wave<A4, SYM, CFG, WX, KS, NB, kXW == 2 ? 1 : -1>(g, wave, lane, st0, st1, st2, sring);
   else
-    gemm_wave<A4, SYM, CFG, WX, KS, NB, false>(g, wave, lane, st0, st1, st2, sring);
+    gemm_wave<A4, SYM, CFG, WX, KS, NB, -1>(g, wave, lane, st0, st1, st2, sring);
 }
 
 constexpr int kMaxDevices = 64;
