@@ -1,5 +1,6 @@
-// K2 for the plans k_gemm1.hip does not take: HQ-DM's single Hadamard
-// (hi/lo weight planes) and SegLinear inputs of 3 or 4 branches. Integer
+// K2 for HQ-DM's single Hadamard (hi/lo weight planes), SegLinear inputs of
+// 3 or 4 branches, and the W8A8 DualScale CFG layers with 144-column tiles
+// (where it measured faster than k_gemm1.hip). Integer
 // GEMM of the activation codes against the weight codes on the int8 matrix
 // cores of gfx950, both DualScale polarity planes in one kernel, with the
 // fp32 epilogue (scales, Hadamard normalisation, CFG combine) fused.
@@ -953,7 +954,11 @@ hipError_t run_mode(const GemmArgs& g, int sym, int cfg, int hs, hipStream_t s) 
     return cfg ? run<A4, false, true, false, true, 8>(g, s)
                : run<A4, false, false, false, true, 8>(g, s);
   }
-  // every other plan runs k_gemm1.hip
+  // Plain int8 weights, 8-bit DualScale activations, CFG, 144-column tiles
+  // (the DiT-XL/2 W8A8 layers): this kernel measured 2-6 % faster than
+  // k_gemm1.hip there. Every other plan runs k_gemm1.hip.
+  if (!A4 && !sym && cfg && g.nks == 1 && g.N % 144 == 0)
+    return run<false, false, true, false, false, 9>(g, s);
   return hipErrorInvalidValue;
 }
 
