@@ -138,8 +138,9 @@ ql_status qlinear_plan(const ql_desc* d, const float* W, void* stream, qlinear_p
  * y = ((float)acc * s) * s_w[n] * (1/B), (float) rounding the exact sum once:
  * X W^T = (1/B) (X H)(H W^T) because H H = B I. */
 
-/* Free a plan's device memory. The caller ensures no enqueued work still
- * uses it (synchronise first). NULL is accepted. */
+/* Free a plan's device memory (weights shared with views are freed with
+ * the last of them). The caller ensures no enqueued work still uses it
+ * (synchronise first). NULL is accepted. */
 ql_status qlinear_plan_destroy(qlinear_plan_t p);
 
 /* Copy a plan's weights out for inspection: w_codes DEVICE int8 [N,K]
@@ -215,6 +216,10 @@ ql_status qlinear_plan_lsb_update(qlinear_plan_t view, qlinear_plan_t base, int3
  *                   (a_bits 4), two 4-bit two's-complement codes per byte:
  *                   element 2j in bits 0-3 and 2j+1 in bits 4-7 of byte j.
  *   act_scales    : DEVICE out fp32 [2S] {s+, s-} per branch, as used.
+ * Method: rotation -- HQ-DM explainer 2.1; DualScale scales and the two
+ * polarity regions -- SegQuant explainer 2.B; per-branch scales -- SegQuant
+ * explainer 2.A (input segmentation); low-bit truncation -- TASQ explainer,
+ * technical summary 2.
  */
 ql_status qlinear_quantize_act(qlinear_plan_t p, const void* X, int32_t M, int32_t lsb_k,
                                const float* static_scales, void* codes, float* act_scales,
@@ -264,6 +269,14 @@ ql_status qlinear_quantize_act_noalloc(qlinear_plan_t p, const void* X, int32_t 
  *                plane 1 = 0; single_hadamard: the exact sum is 128 * plane 0
  *                + plane 1, the products with the hi and lo planes). For
  *                parity checks; costs extra stores.
+ * Errors besides the common ones: QL_ERR_UNSUPPORTED when M > 2^23, when
+ * codes or weights reach 2 GiB, or when a 128-row block of Y does (N * 512
+ * bytes >= 2^31: output offsets are 32-bit).
+ * Method: the two products and their fused rescaled sum -- SegQuant
+ * explainer 2.B; per-branch parts -- SegQuant explainer 2.A; normalisation
+ * 1/B -- HQ-DM explainer 2.1; CFG combine -- "Closing the Null Space"
+ * explainer, problem statement; a view's weight depth -- TASQ explainer,
+ * technical summary 2.
  */
 ql_status qlinear_gemm(qlinear_plan_t p, const void* codes, const float* act_scales, int32_t M,
                        int32_t cfg, float w, float* Y, int32_t* acc_dbg, void* stream);

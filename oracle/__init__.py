@@ -26,7 +26,9 @@ import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "oracle.cpp")
-_LIB = os.path.join(_HERE, "liboracle.so")
+# ORACLE_LIB selects another build of the same source (the sanitizer build).
+_LIB = os.environ.get("ORACLE_LIB") or os.path.join(_HERE, "liboracle.so")
+_SAN_LIB = os.path.join(_HERE, "liboracle_san.so")
 
 DUAL, SYMMETRIC = 0, 1
 W_TENSOR, W_SEGMENT, W_CHANNEL = 0, 1, 2
@@ -34,15 +36,23 @@ _WMODES = {"tensor": W_TENSOR, "segment": W_SEGMENT, "channel": W_CHANNEL}
 _AMODES = {"dual": DUAL, "symmetric": SYMMETRIC}
 
 
-def build(force: bool = True) -> str:
-    """Compile liboracle.so with the host compiler (plain C++17)."""
-    if not force and os.path.exists(_LIB):
-        return _LIB
-    cmd = ["g++", "-std=c++17", "-O2", "-ffp-contract=off", "-fno-fast-math",
-           "-fPIC", "-shared", "-Wall", "-Wextra", "-o", _LIB + ".tmp", _SRC]
+def build(force: bool = True, sanitize: bool = False) -> str:
+    """Compile liboracle.so with the host compiler (plain C++17); with
+    sanitize, liboracle_san.so under AddressSanitizer and
+    UndefinedBehaviorSanitizer (any report aborts), for running the pins
+    under them with the ASan runtime preloaded."""
+    out = _SAN_LIB if sanitize else os.path.join(_HERE, "liboracle.so")
+    if not force and os.path.exists(out):
+        return out
+    flags = ["-O2"]
+    if sanitize:
+        flags = ["-O1", "-g", "-fno-omit-frame-pointer", "-fsanitize=address,undefined",
+                 "-fno-sanitize-recover=all"]
+    cmd = (["g++", "-std=c++17"] + flags + ["-ffp-contract=off", "-fno-fast-math",
+           "-fPIC", "-shared", "-Wall", "-Wextra", "-o", out + ".tmp", _SRC])
     subprocess.run(cmd, check=True)
-    os.replace(_LIB + ".tmp", _LIB)
-    return _LIB
+    os.replace(out + ".tmp", out)
+    return out
 
 
 _lib = None
@@ -52,7 +62,7 @@ def lib() -> ctypes.CDLL:
     global _lib
     if _lib is None:
         if not os.path.exists(_LIB):
-            build(force=False)
+            build(force=False, sanitize=_LIB == _SAN_LIB)
         L = ctypes.CDLL(_LIB)
         P = ctypes.c_void_p
         I32, I64, F32 = ctypes.c_int32, ctypes.c_int64, ctypes.c_float
