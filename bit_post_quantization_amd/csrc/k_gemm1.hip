@@ -130,47 +130,6 @@ __device__ __forceinline__ v4i positive(v4i c) {
   return p;
 }
 
-// TASQ's truncation of four int8 codes (|c| <= 127): the kk low bits of each
-// magnitude cleared, sign kept, i.e. rounding toward zero to a multiple of
-// 2^kk. A negative byte gets 2^kk - 1 added before its low bits are
-// cleared; the add runs on the low 7 bits (at most 127 + 127, so no carry
-// leaves a byte) and the sign bit is put back by exclusive or. The bias
-// comes from a byte table: v_perm_b32 with selector 0 or 1 per byte (the
-// byte's sign bit) picks byte 0 (= 0) or byte 1 (= 2^kk - 1) of lut. Five
-// VALU instructions.
-// lut = (2^kk - 1) << 8; keep = the byte ~(2^kk - 1) in every byte.
-__device__ __forceinline__ uint32_t trunc_mag4(uint32_t b, uint32_t lut, uint32_t keep) {
-  const uint32_t h = b & 0x80808080u;
-  const uint32_t bias = __builtin_amdgcn_perm(0u, lut, h >> 7);
-  uint32_t s;
-  asm("v_xad_u32 %0, %1, %2, %3" : "=v"(s) : "v"(b), "v"(h), "v"(bias));  // (b ^ h) + bias
-  return (s ^ h) & keep;
-}
-
-// Nine floats at p, p + 16, ..., p + 128 (LDS), read in one asm block that
-// waits for them itself. The scale ring is written by DMA, and the compiler,
-// unable to tell which DMA wrote it, would otherwise wait for every load in
-// flight before a plain LDS read of it; the ring entry read here was written
-// tiles earlier and published by the step barriers since.
-__device__ __forceinline__ void lds_read9_stride16(const float* p, float* v) {
-  const uint32_t a = (uint32_t)reinterpret_cast<uintptr_t>(p);  // LDS offset of a shared pointer
-  asm volatile(
-      "ds_read_b32 %0, %9\n\t"
-      "ds_read_b32 %1, %9 offset:64\n\t"
-      "ds_read_b32 %2, %9 offset:128\n\t"
-      "ds_read_b32 %3, %9 offset:192\n\t"
-      "ds_read_b32 %4, %9 offset:256\n\t"
-      "ds_read_b32 %5, %9 offset:320\n\t"
-      "ds_read_b32 %6, %9 offset:384\n\t"
-      "ds_read_b32 %7, %9 offset:448\n\t"
-      "ds_read_b32 %8, %9 offset:512\n\t"
-      "s_waitcnt lgkmcnt(0)"
-      : "=&v"(v[0]), "=&v"(v[1]), "=&v"(v[2]), "=&v"(v[3]), "=&v"(v[4]), "=&v"(v[5]),
-        "=&v"(v[6]), "=&v"(v[7]), "=&v"(v[8])
-      : "v"(a)
-      : "memory");
-}
-
 // y from the two accumulators in the documented order, no contraction.
 template <bool SYM>
 __device__ __forceinline__ float epi_part(int accp, int accn, float sp, float sn, float sw) {

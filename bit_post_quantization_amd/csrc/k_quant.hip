@@ -22,6 +22,8 @@
 // fed by a concatenation quantizes each branch apart) the same two kernels
 // keep one maximum pair and one scale pair per branch; a unit's branch
 // follows from its column, tracked incrementally along the stream.
+#include <type_traits>
+
 #include "ql_device.h"
 #include "ql_kernels.h"
 
@@ -198,30 +200,71 @@ __device__ __forceinline__ void scales_from_partials(const QuantArgs& a, int j, 
   }
 }
 
-// Codes of the four values of a unit; the same codes as quant_dual (round
-// half even of the correctly rounded quotient v / s, clamped), computed as
-// t = v * (1/s): the quotient and t differ by less than |t| * 2^-22, so
-// wherever t lies farther than |t| * 2^-20 + 2^-20 from every half-integer
-// both round to the same integer. Units with a value closer than that (and
-// non-finite t) are redone with the division; that is rare and
-// wave-uniform work is skipped when no lane needs it. With r = 0 for a zero
-// scale, t = 0 and the code is 0 as the definition requires; the sign of t
-// follows v, so one symmetric clamp serves both polarity regions.
-__device__ __forceinline__ void quant_unit(const float (&e)[4], float sp, float sn, float rp,
-                                           float rn, float qa, int (&c)[4]) {
+// Codes of the four values of a unit, packed one per byte (element i in
+// byte i); the same codes as quant_dual (round half even of the correctly
+// rounded quotient v / s, clamped), computed from t = v * (1/s): the
+// quotient and t differ by less than |t| * 2^-22, so wherever t lies
+// farther than |t| * 2^-20 + 2^-20 from every half-integer both round to
+// the same integer. Units with a value closer than that (and non-finite t)
+// are redone with the division; that is rare and wave-uniform work is
+// skipped when no lane needs it. Rounding: m = t + 1.5 * 2^23 is t rounded
+// half to even into the units of [2^23, 2^24) (the sum's even mantissas are
+// the even integers), so m - 1.5 * 2^23 = rint(t) for |t| < 2^22, and after
+// clamping m to 1.5 * 2^23 +- qa the code is the low byte of m's bits (the
+// mantissa is 0x400000 + code). With r = 0 for a zero scale, t = 0 and the
+// code is 0 as the definition requires; the sign of t follows v, so one
+// symmetric clamp serves both polarity regions. SYM: one scale.
+template <bool SYM>
+__device__ __forceinline__ uint32_t quant_pack(const float (&e)[4], float sp, float sn, float rp,
+                                               float rn, float qa) {
+  constexpr float kMagic = 12582912.0f;  // 1.5 * 2^23
+  float m[4];
   bool slow = false;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const float v = e[i];
-    const float t = v * (v >= 0.0f ? rp : rn);
-    const float r = rintf(t);
+    const float t = v * (SYM ? rp : (v >= 0.0f ? rp : rn));
+    const float s = t + kMagic;
+    const float r = s - kMagic;
     const float z = fmaf(fabsf(t), 0x1p-20f, fabsf(t - r));
     slow |= !(z < 0x1.fffcp-2f);  // 0.5 - 2^-19
-    c[i] = (int)__builtin_amdgcn_fmed3f(r, -qa, qa);
+    m[i] = __builtin_amdgcn_fmed3f(s, kMagic - qa, kMagic + qa);
   }
   if (slow) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) c[i] = quant_dual(e[i], sp, sn, qa);
+    for (int i = 0; i < 4; ++i) m[i] = kMagic + (float)quant_dual(e[i], sp, sn, qa);
+  }
+  // bytes: [m0.b0, m1.b0, 0, 0] | [0, 0, m2.b0, m3.b0]
+  const uint32_t lo = __builtin_amdgcn_perm(__float_as_uint(m[1]), __float_as_uint(m[0]), 0x0c0c0400u);
+  const uint32_t hi = __builtin_amdgcn_perm(__float_as_uint(m[3]), __float_as_uint(m[2]), 0x04000c0cu);
+  return lo | hi;
+}
+
+// TASQ truncation of a packed unit (k = lsb_k low magnitude bits cleared),
+// then the store: 4 bytes, or (4-bit codes) two bytes of two nibbles each,
+// element 2j in the low nibble of byte j.
+struct LsbMask {
+  bool on;
+  uint32_t lut, keep;
+  __device__ explicit LsbMask(int keep_mask) {
+    const int k = keep_mask == -1 ? 0 : __builtin_ctz((uint32_t)keep_mask);
+    on = k > 0;
+    lut = ((1u << k) - 1u) << 8;
+    keep = 0x01010101u * (0xFFu & (uint32_t)keep_mask);
+  }
+};
+
+template <bool A4>
+__device__ __forceinline__ void store_unit(const __amdgpu_buffer_rsrc_t& rc, uint32_t off,
+                                           uint32_t p, const LsbMask& mk) {
+  if (mk.on) p = trunc_mag4(p, mk.lut, mk.keep);
+  if constexpr (A4) {
+    const uint32_t q = p & 0x0F0F0F0Fu;
+    const uint32_t r = q | (q >> 4);  // byte 0 = c0 | c1 << 4, byte 2 = c2 | c3 << 4
+    __builtin_amdgcn_raw_buffer_store_b16((unsigned short)__builtin_amdgcn_perm(0u, r, 0x0c0c0200u),
+                                          rc, off, 0, 0);
+  } else {
+    __builtin_amdgcn_raw_buffer_store_b32(p, rc, off, 0, 0);
   }
 }
 
@@ -252,6 +295,7 @@ __global__ __launch_bounds__(kThreads) void k1_quantize(QuantArgs a) {
   }
   const int cstep = KS ? kThreads % a.k_units : 0;
   constexpr uint32_t kCodeBytes = A4 ? 2 : 4;
+  const LsbMask mk(a.keep_mask);
   const int64_t nchunks = (a.nunits + kChunk - 1) / kChunk;
   for (int64_t ch = blockIdx.x; ch < nchunks; ch += gridDim.x) {
     float e[kUnroll][4];
@@ -280,24 +324,207 @@ __global__ __launch_bounds__(kThreads) void k1_quantize(QuantArgs a) {
         }
         col = next_col(a, col, cstep);
       }
-      int c[4];
-      quant_unit(e[u], sp, sn, rp, rn, a.qa, c);
-      if (a.keep_mask != -1) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) c[i] = truncate_lsb(c[i], a.keep_mask);
-      }
-      const uint32_t off = (uint32_t)(u * kThreads + threadIdx.x) * kCodeBytes;
-      if constexpr (A4) {
-        const uint32_t p = (c[0] & 0xF) | ((c[1] & 0xF) << 4) | ((c[2] & 0xF) << 8) |
-                           ((c[3] & 0xF) << 12);
-        __builtin_amdgcn_raw_buffer_store_b16((unsigned short)p, rc, off, 0, 0);
-      } else {
-        const uint32_t p = (c[0] & 0xFF) | ((c[1] & 0xFF) << 8) | ((c[2] & 0xFF) << 16) |
-                           ((uint32_t)(c[3] & 0xFF) << 24);
-        __builtin_amdgcn_raw_buffer_store_b32(p, rc, off, 0, 0);
-      }
+      const uint32_t p = a.sym ? quant_pack<true>(e[u], sp, sn, rp, rn, a.qa)
+                               : quant_pack<false>(e[u], sp, sn, rp, rn, a.qa);
+      store_unit<A4>(rc, (uint32_t)(u * kThreads + threadIdx.x) * kCodeBytes, p, mk);
     }
   }
+}
+
+// ---- One pass, for tensors that fit on chip (dynamic scales, no input
+// branches). One workgroup per compute unit holds its slice of X in
+// registers (up to kFUnits units per lane) and publishes its partial maxima;
+// workgroup 0 gathers them and publishes the tensor's maxima; every
+// workgroup then quantizes from registers: X is read once (5 bytes per fp32
+// element moved in all, instead of 9). Every wait is bounded: a workgroup
+// that gives up (only possible if the grid was not all resident) scans X
+// for the maxima itself, so the kernel always ends and its codes are always
+// those of the two-pass path.
+constexpr int kFThreads = 512;               // 8 waves, 2 per SIMD
+constexpr int kFWaves = kFThreads / kWave;
+constexpr int kFUnits = 40;                  // units per lane held in registers, at most
+constexpr uint32_t kFSpin = 1u << 18;        // barrier polls before scanning X
+
+template <bool BF16>
+__device__ __forceinline__ void load_unit(const __amdgpu_buffer_rsrc_t& r, uint32_t off,
+                                          float (&e)[4]) {
+  if constexpr (BF16) {
+    const v2u v = __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0);
+    e[0] = __uint_as_float(v.x << 16);
+    e[1] = __uint_as_float(v.x & 0xFFFF0000u);
+    e[2] = __uint_as_float(v.y << 16);
+    e[3] = __uint_as_float(v.y & 0xFFFF0000u);
+  } else {
+    const v4u v = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
+    e[0] = __uint_as_float(v.x);
+    e[1] = __uint_as_float(v.y);
+    e[2] = __uint_as_float(v.z);
+    e[3] = __uint_as_float(v.w);
+  }
+}
+
+// Fold four values into the maxima pair (bit patterns, as k1_reduce keeps them).
+__device__ __forceinline__ void max4(const float (&e)[4], uint32_t& mp, uint32_t& mn) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const uint32_t b = __float_as_uint(e[i]);
+    mp = (uint32_t)max((int32_t)mp, (int32_t)b);
+    mn = max(mn, b);
+  }
+}
+
+// Workgroup-wide max of (mp, mn) (mn as a magnitude), returned to every thread.
+__device__ __forceinline__ void block_max2(uint32_t& mp, uint32_t& mn, uint32_t (&sm)[2][kFWaves]) {
+  const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
+  mp = wave_max_u32(mp);
+  mn = wave_max_u32(mn);
+  if (lane == 0) {
+    sm[0][wave] = mp;
+    sm[1][wave] = mn;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int w = 0; w < kFWaves; ++w) {
+    mp = max(mp, sm[0][w]);
+    mn = max(mn, sm[1][w]);
+  }
+  __syncthreads();
+}
+
+template <bool BF16, int HB, bool A4>
+__global__ __launch_bounds__(kFThreads, 1) void k1_fused(QuantArgs a, int U) {
+  __shared__ uint32_t sm[2][kFWaves];
+  const int tid = threadIdx.x, lane = tid & (kWave - 1);
+  const int G = gridDim.x, b = blockIdx.x;
+  constexpr uint32_t kUnitBytes = BF16 ? 8 : 16;
+  const int64_t span = (int64_t)U * kFThreads;
+  const int64_t first = (int64_t)b * span;
+  const int64_t left = a.nunits - first;
+  const uint32_t here = (uint32_t)(left <= 0 ? 0 : (left < span ? left : span));
+  const __amdgpu_buffer_rsrc_t rx =
+      buffer_rsrc(reinterpret_cast<const uint8_t*>(a.X) + first * kUnitBytes, here * kUnitBytes);
+  // Unit u of this lane: first + u * kFThreads + tid (consecutive lanes on
+  // consecutive units; units past the end read as zeros).
+  float e[kFUnits][4];
+#pragma unroll
+  for (int u = 0; u < kFUnits; ++u) {
+    if (u < U) {
+      load_unit<BF16>(rx, (uint32_t)(u * kFThreads + tid) * kUnitBytes, e[u]);
+    } else {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) e[u][i] = 0.0f;
+    }
+  }
+  if constexpr (HB > 0) {
+#pragma unroll
+    for (int u = 0; u < kFUnits; ++u)
+      if (u < U) fwht_block<HB>(e[u], lane);
+  }
+  uint32_t mp = 0, mn = 0x80000000u;  // +0 and -0: zeros never win
+#pragma unroll
+  for (int u = 0; u < kFUnits; ++u) max4(e[u], mp, mn);
+  mn &= 0x7FFFFFFFu;
+  block_max2(mp, mn, sm);
+
+  // Exchange: publish this workgroup's maxima; workgroup 0 gathers all of
+  // them and publishes the tensor's; the others wait for that.
+  GridSync* gs = &a.ws->sync;
+  const uint64_t tag = (uint64_t)a.seq << 32;
+  __shared__ uint32_t got[3];
+  if (tid == 0) {
+    __hip_atomic_store(&gs->word[0][b], tag | mp, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_store(&gs->word[1][b], tag | mn, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+  bool ok = false;
+  uint32_t gp = 0, gn = 0;
+  if (b == 0) {
+    for (uint32_t it = 0; it < kFSpin; ++it) {
+      bool mine = true;
+      if (tid < G) {
+        const uint64_t w0 = __hip_atomic_load(&gs->word[0][tid], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        const uint64_t w1 = __hip_atomic_load(&gs->word[1][tid], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        mine = (w0 & ~0xFFFFFFFFull) == tag && (w1 & ~0xFFFFFFFFull) == tag;
+        gp = (uint32_t)w0;
+        gn = (uint32_t)w1;
+      }
+      if (__syncthreads_and(mine)) {
+        ok = true;
+        break;
+      }
+      __builtin_amdgcn_s_sleep(2);
+    }
+  } else {
+    if (tid == 0) {
+      got[0] = 0;
+      for (uint32_t it = 0; it < kFSpin; ++it) {
+        const uint64_t r0 = __hip_atomic_load(&gs->result[0], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        const uint64_t r1 = __hip_atomic_load(&gs->result[1], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if ((r0 & ~0xFFFFFFFFull) == tag && (r1 & ~0xFFFFFFFFull) == tag) {
+          got[0] = 1;
+          got[1] = (uint32_t)r0;
+          got[2] = (uint32_t)r1;
+          break;
+        }
+        __builtin_amdgcn_s_sleep(4);
+      }
+    }
+    __syncthreads();
+    ok = got[0] != 0;
+    // every thread takes the tensor's maxima (the max below leaves them as they are)
+    gp = ok ? got[1] : 0;
+    gn = ok ? got[2] : 0;
+  }
+  if (!ok) {
+    // Fallback: the maxima of the whole tensor, read here.
+    if (tid == 0) __hip_atomic_fetch_add(&gs->fallbacks, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const __amdgpu_buffer_rsrc_t rall = buffer_rsrc(a.X, (uint32_t)(a.nunits * kUnitBytes));
+    uint32_t fp = 0, fn = 0x80000000u;
+    for (int64_t i = tid; i < a.nunits; i += kFThreads) {
+      float f[4];
+      load_unit<BF16>(rall, (uint32_t)i * kUnitBytes, f);
+      if constexpr (HB > 0) fwht_block<HB>(f, lane);
+      max4(f, fp, fn);
+    }
+    gp = fp;
+    gn = fn & 0x7FFFFFFFu;
+  }
+  block_max2(gp, gn, sm);
+  if (b == 0 && tid == 0) {  // the tensor's maxima, for the other workgroups
+    __hip_atomic_store(&gs->result[0], tag | gp, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_store(&gs->result[1], tag | gn, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+  const float mx = __uint_as_float(gp), mnv = __uint_as_float(gn);
+  float sp, sn;
+  if (a.sym) {
+    sp = (mx > mnv ? mx : mnv) / a.qa;
+    sn = sp;
+  } else {
+    sp = mx / a.qa;
+    sn = mnv / a.qa;
+  }
+  if (b == 0 && tid == 0) {
+    a.act_scales[0] = sp;
+    a.act_scales[1] = sn;
+  }
+  const float rp = sp > 0.0f ? 1.0f / sp : 0.0f;
+  const float rn = sn > 0.0f ? 1.0f / sn : 0.0f;
+  constexpr uint32_t kCodeBytes = A4 ? 2 : 4;
+  const __amdgpu_buffer_rsrc_t rc =
+      buffer_rsrc(reinterpret_cast<uint8_t*>(a.codes) + first * kCodeBytes, here * kCodeBytes);
+  const LsbMask mk(a.keep_mask);
+  auto quant_all = [&](auto symc) __attribute__((always_inline)) {
+    constexpr bool SYM = decltype(symc)::value;
+#pragma unroll
+    for (int u = 0; u < kFUnits; ++u) {
+      if (u < U)
+        store_unit<A4>(rc, (uint32_t)(u * kFThreads + tid) * kCodeBytes,
+                       quant_pack<SYM>(e[u], sp, sn, rp, rn, a.qa), mk);
+    }
+  };
+  if (a.sym)
+    quant_all(std::true_type{});
+  else
+    quant_all(std::false_type{});
 }
 
 int chunks_of(int64_t nunits) {
@@ -312,8 +539,35 @@ int balanced_grid(int nch, int cap) {
   return (nch + per - 1) / per;
 }
 
+// One-pass launch when the tensor fits in the registers of one workgroup
+// per compute unit (and no branches, dynamic scales, HB 0 or 128): returns
+// false to let the caller run the two passes.
+template <bool BF16, int HB, bool A4>
+bool run_fused(const QuantArgs& a, hipStream_t s, hipError_t& e) {
+  if constexpr (HB != 0 && HB != 128) {
+    return false;
+  } else {
+    if (a.static_scales || a.nks != 1 || a.nunits <= 0 || a.seq == 0) return false;
+    int dev = 0, cus = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+      return false;
+    const int64_t per = (int64_t)cus * kFThreads;
+    const int64_t U = (a.nunits + per - 1) / per;
+    if (U > kFUnits || cus > kMaxReduceBlocks) return false;
+    const int G = (int)((a.nunits + U * kFThreads - 1) / (U * kFThreads));
+    hipLaunchKernelGGL((k1_fused<BF16, HB, A4>), dim3(G), dim3(kFThreads), 0, s, a, (int)U);
+    e = hipGetLastError();
+    return true;
+  }
+}
+
 template <bool BF16, int HB, bool A4, bool KS>
 hipError_t run_ks(QuantArgs a, hipStream_t s) {
+  if constexpr (!KS) {
+    hipError_t e = hipSuccess;
+    if (run_fused<BF16, HB, A4>(a, s, e)) return e;
+  }
   const int nch = chunks_of(a.nunits);
   const int g = balanced_grid(nch, kQuantBlocks);
   if (!a.static_scales) {

@@ -11,9 +11,24 @@ namespace ql {
 // order makes them visible; nothing needs clearing between calls).
 constexpr int kMaxReduceBlocks = 1024;
 constexpr int kMaxKSeg = 4;  // input branches (SegLinear input segmentation)
+// Grid exchange of the one-pass quantizer. Workgroup b writes its partial
+// maxima as word[j][b] = (sequence number << 32) | bits (j = 0: max, 1: the
+// most negative value's magnitude); workgroup 0 waits for every word of the
+// grid to carry the call's number, folds them, and writes the maxima of the
+// tensor the same way into result[j], which the other workgroups wait for.
+// 64-bit words are written and read whole, so a tag and its value arrive
+// together and no fence is needed; nothing is reset between calls. Zero at
+// allocation (sequence numbers start at 1).
+struct GridSync {
+  uint64_t word[2][kMaxReduceBlocks];
+  uint64_t result[2];
+  uint32_t fallbacks;  // workgroups that stopped waiting and scanned X themselves
+  uint32_t pad[59];
+};
 struct ReduceWs {
   // per branch: bits of max(+0, max x), max(+0, -min x)
   uint32_t part[kMaxKSeg][2][kMaxReduceBlocks];
+  GridSync sync;
 };
 
 struct QuantArgs {
@@ -30,6 +45,7 @@ struct QuantArgs {
   int nks;                   // input branches (1: one scale pair for the tensor)
   int k_units;               // K / 4
   int ks_units[kMaxKSeg];    // branch starts in units (k_j / 4); unused ones = k_units
+  uint32_t seq;              // call sequence number (one-pass quantizer's barrier), >= 1
 };
 
 struct GemmArgs {

@@ -5,6 +5,7 @@
 
 #include <hip/hip_runtime.h>
 
+#include <atomic>
 #include <cstdarg>
 #include <cstdio>
 #include <memory>
@@ -208,10 +209,11 @@ ql_status enqueue_lsb(struct qlinear_plan* view, const struct qlinear_plan* base
 
 // Reduction workspace of qlinear_quantize_act_noalloc: one copy per device,
 // holding every partial maximum a call can write (kMaxKSeg branches x
-// kMaxReduceBlocks pairs, 32 KiB). Host code never passes `scratch` itself
-// to a kernel (that name is a host-side stand-in): it passes the device
-// address looked up once per device below.
-static __device__ __align__(256) uint8_t scratch[sizeof(ql::ReduceWs)];
+// kMaxReduceBlocks pairs, 32 KiB) and the one-pass quantizer's barrier flags
+// (4 KiB; zero when the library is loaded). Host code never passes `scratch`
+// itself to a kernel (that name is a host-side stand-in): it passes the
+// device address looked up once per device below.
+static __device__ __align__(256) uint8_t scratch[sizeof(ql::ReduceWs)] = {};
 
 namespace {
 
@@ -233,6 +235,15 @@ hipError_t scratch_address(int dev, void** out) {
   }
   *out = g_scratch_ptr[dev];
   return hipSuccess;
+}
+
+// Sequence numbers of quantize calls, never 0 (the one-pass quantizer's
+// barrier flags start at 0).
+std::atomic<uint32_t> g_seq{0};
+uint32_t next_seq() {
+  uint32_t v = g_seq.fetch_add(1) + 1;
+  while (v == 0) v = g_seq.fetch_add(1) + 1;
+  return v;
 }
 
 // Shared body of qlinear_quantize_act and its no-allocation variant: `ws`
@@ -264,6 +275,7 @@ ql_status quantize_impl(qlinear_plan_t p, const void* X, int32_t M, int32_t lsb_
   a.nks = p->nks;
   a.k_units = p->d.K / 4;
   for (int j = 0; j < ql::kMaxKSeg; ++j) a.ks_units[j] = j < p->nks ? p->kseg[j] / 4 : a.k_units;
+  a.seq = next_seq();
   hipError_t e = ql::launch_quantize(a, bf16, p->d.hadamard_block, p->d.a_bits == 4,
                                      reinterpret_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "launching quantize");
@@ -348,6 +360,7 @@ ql_status qlinear_plan(const ql_desc* d, const float* W, void* stream, qlinear_p
   if (p->packed4) QL_TRY(hipMalloc(&codes8, wbytes), "allocating unpacked weight codes");
   QL_TRY(dev_alloc(p->sw, (size_t)p->nks * N * sizeof(float)), "allocating weight scales");
   QL_TRY(hipMalloc(&p->ws, sizeof(ql::ReduceWs)), "allocating reduction workspace");
+  QL_TRY(hipMemsetAsync(p->ws, 0, sizeof(ql::ReduceWs), s), "clearing reduction workspace");
   QL_TRY(hipMalloc(&rowmax, N * sizeof(uint32_t)), "allocating row maxima");
   QL_TRY(alloc_ypart(p), "allocating partial-sum workspace");
   // Offsets that define the scale groups: the given segments for
@@ -424,7 +437,9 @@ ql_status qlinear_plan_lsb_view(qlinear_plan_t base, int32_t w_lsb_k, void* stre
     v->wq = base->wq;
     v->sw = base->sw;
     v->w_lsb_k = w_lsb_k > base->w_lsb_k ? w_lsb_k : base->w_lsb_k;
-    const hipError_t e = hipMalloc(&v->ws, sizeof(ql::ReduceWs));
+    hipError_t e = hipMalloc(&v->ws, sizeof(ql::ReduceWs));
+    if (e == hipSuccess) e = hipMemsetAsync(v->ws, 0, sizeof(ql::ReduceWs), s);
+    if (e == hipSuccess) e = hipStreamSynchronize(s);
     if (e != hipSuccess) {
       free_plan(v);
       return hip_fail(e, "allocating view plan");
@@ -437,6 +452,7 @@ ql_status qlinear_plan_lsb_view(qlinear_plan_t base, int32_t w_lsb_k, void* stre
   hipError_t e = dev_alloc(v->wq, gbytes);
   if (e == hipSuccess) e = dev_alloc(v->sw, (size_t)base->nks * base->d.N * sizeof(float));
   if (e == hipSuccess) e = hipMalloc(&v->ws, sizeof(ql::ReduceWs));
+  if (e == hipSuccess) e = hipMemsetAsync(v->ws, 0, sizeof(ql::ReduceWs), s);
   if (e == hipSuccess) e = alloc_ypart(v);
   if (e == hipSuccess && base->d.single_hadamard) {
     e = dev_alloc(v->wint, wbytes);
