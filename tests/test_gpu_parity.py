@@ -505,6 +505,40 @@ def test_codes_at_rounding_boundaries(torch, a_bits):
     assert bad.size == 0, f"{bad.size} codes differ, first at {bad[:5]}: x={flat[bad[:5]]}"
 
 
+
+@pytest.mark.parametrize("a_bits,B,x_dtype,lsb_k,a_scale", [
+    (8, 0, "f32", 0, "dual"), (4, 128, "bf16", 1, "dual"), (8, 128, "f32", 2, "symmetric")])
+def test_one_pass_quantizer_limits(torch, a_bits, B, x_dtype, lsb_k, a_scale):
+    # Dynamic scales run in one pass when X fits in 40 units of 4 values per
+    # lane, 512 lanes per CU: the largest such tensor (its last workgroup
+    # ragged) and one row more (two passes) must both give the oracle's
+    # scales and codes.
+    from bit_post_quantization_amd import QuantLinear
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    K, N = 4608, 16
+    M1 = (40 * cus * 512 * 4) // K
+    W = synth.weight_normal(44, "onepass/W", N, K)
+    ql = QuantLinear(_dev(torch, W), a_bits=a_bits, hadamard_block=B, x_dtype=x_dtype,
+                     a_scale=a_scale)
+    for M in (M1, M1 + 1):
+        say(f"[case] one-pass limit M={M} K={K} a{a_bits} B={B} {x_dtype} k={lsb_k} {a_scale}")
+        X = synth.silu_normal(44, f"onepass/{M}/{a_bits}/{B}", M, K)
+        if x_dtype == "bf16":
+            X = synth.f32_to_bf16_bits(X)
+        Xd = _dev(torch, X) if x_dtype == "f32" else _dev(torch, X.view(np.int16))
+        codes_d, s_d = ql.quantize(Xd, lsb_k=lsb_k)
+        torch.cuda.synchronize()
+        s_g = s_d.cpu().numpy()
+        codes_g = unpack_codes(codes_d.cpu().numpy(), K, a_bits)
+        del Xd, codes_d
+        x32 = oracle.bf16_to_f32(X) if x_dtype == "bf16" else X
+        x_rot = oracle.rotate(x32, B) if B else x32
+        s_o = oracle.act_scales(x_rot, a_bits, a_scale)
+        assert np.array_equal(s_g.view(np.uint32), s_o.view(np.uint32)), f"scales {s_g} vs {s_o}"
+        st = compare_codes(codes_g, oracle.quantize_act(x_rot, s_o, a_bits, lsb_k), x_rot, s_o)
+        say(f"  codes: {st}")
+        assert_codes(st)
+
 def test_static_scales(torch):
     M, K, N = 64, 256, 80
     X = synth.silu_normal(4, "static/X", M, K)
