@@ -312,6 +312,47 @@ __device__ __forceinline__ void schedule_step() {
   sched_groups<0, NBW, NREADS, (VALU_PER_GROUP + NBW - 1) / NBW, DUAL>();
 }
 
+// n (4, 5 or 6) floats at p, p + 16, ... (LDS), read in one asm block that
+// waits for them itself. The scale ring is written by DMA, and the compiler,
+// unable to tell which DMA wrote it, would otherwise wait for every load in
+// flight before a plain LDS read of it; the ring entry read here was written
+// steps earlier and published by the step barriers since.
+template <int N>
+__device__ __forceinline__ void lds_read_stride16(const float* p, float* v) {
+  static_assert(N >= 4 && N <= 6, "scale reads");
+  const uint32_t a = (uint32_t)reinterpret_cast<uintptr_t>(p);  // LDS offset of a shared pointer
+  if constexpr (N == 4) {
+    asm volatile(
+        "ds_read_b32 %0, %4\n\tds_read_b32 %1, %4 offset:64\n\t"
+        "ds_read_b32 %2, %4 offset:128\n\tds_read_b32 %3, %4 offset:192\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(v[0]), "=&v"(v[1]), "=&v"(v[2]), "=&v"(v[3])
+        : "v"(a)
+        : "memory");
+  } else if constexpr (N == 5) {
+    asm volatile(
+        "ds_read_b32 %0, %5\n\tds_read_b32 %1, %5 offset:64\n\t"
+        "ds_read_b32 %2, %5 offset:128\n\tds_read_b32 %3, %5 offset:192\n\t"
+        "ds_read_b32 %4, %5 offset:256\n\ts_waitcnt lgkmcnt(0)"
+        : "=&v"(v[0]), "=&v"(v[1]), "=&v"(v[2]), "=&v"(v[3]), "=&v"(v[4])
+        : "v"(a)
+        : "memory");
+  } else {
+    asm volatile(
+        "ds_read_b32 %0, %6\n\tds_read_b32 %1, %6 offset:64\n\t"
+        "ds_read_b32 %2, %6 offset:128\n\tds_read_b32 %3, %6 offset:192\n\t"
+        "ds_read_b32 %4, %6 offset:256\n\tds_read_b32 %5, %6 offset:320\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(v[0]), "=&v"(v[1]), "=&v"(v[2]), "=&v"(v[3]), "=&v"(v[4]), "=&v"(v[5])
+        : "v"(a)
+        : "memory");
+  }
+}
+
+// Plain tiles (no single Hadamard, no input branches) take their weight
+// scales from a ring of kScaleRing tile entries of 256 floats in LDS.
+constexpr int kScaleRing = 8;
+
 // The work of one wave. CG (column group) fixes at compile time how many
 // weight fragments the wave multiplies and TW whether it also moves weight
 // pair w + 8, so a step's body has no branches and every step issues the
@@ -319,7 +360,8 @@ __device__ __forceinline__ void schedule_step() {
 // waits below that each LDS read finds its data landed.
 template <bool A4, bool SYM, bool CFG, bool HS, bool KS, int NB, int CG, bool TW>
 __device__ __forceinline__ void gemm_wave(const GemmArgs& g, int wave, int lane, uint8_t* st0,
-                                          uint8_t* st1, uint8_t* st2, uint8_t* st3) {
+                                          uint8_t* st1, uint8_t* st2, uint8_t* st3,
+                                          float* sring) {
   using Lay = Layout<A4, NB>;
   using IA = FragIO<A4>;
   using IW = FragIO<false>;  // weights are int8 codes (4-bit ones expanded by the plan)
@@ -343,6 +385,8 @@ __device__ __forceinline__ void gemm_wave(const GemmArgs& g, int wave, int lane,
 
   const __amdgpu_buffer_rsrc_t ra = make_rsrc(g.A, (uint32_t)((int64_t)g.M * g.lda));
   const __amdgpu_buffer_rsrc_t rw = make_rsrc(g.W, (uint32_t)((int64_t)g.N * g.ldw));
+  constexpr bool kRing = !HS && !KS;  // weight scales through the LDS ring
+  const __amdgpu_buffer_rsrc_t rs = make_rsrc(g.w_scales, (uint32_t)g.Nout * 4u);
 
   auto coords = [&](int ti, int& m0, int& n0) __attribute__((always_inline)) {
     const int t = tl.at(ti);
@@ -371,9 +415,21 @@ __device__ __forceinline__ void gemm_wave(const GemmArgs& g, int wave, int lane,
   // scalar operand of the loads.
   int iss_ti = 0, iss_k = 0;
   unsigned av[IA::kLoads], wv[2][IW::kLoads];
+  // Entering a tile (kStages steps ahead of its MFMAs, so at most kStages
+  // tiles ahead of the epilogue that reads the entry), wave 0 also moves the
+  // tile's 16*NB weight scales into entry ti % kScaleRing of the scale ring
+  // (16 bytes per lane; columns past N read as 0).
   auto enter_tile = [&](int ti) __attribute__((always_inline)) {
     int m0, n0;
     coords(ti, m0, n0);
+    if constexpr (kRing) {
+      static_assert(kScaleRing > kStages, "scale ring entries outlive the stream's lead");
+      if (wave == 0) {
+        const unsigned v = 16u * (unsigned)lane < 4u * (unsigned)BN ? 16u * (unsigned)lane : kOOB;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            rs, (lds_void*)(sring + (ti % kScaleRing) * 256), 16, v, 4u * (unsigned)n0, 0, 0);
+      }
+    }
 #pragma unroll
     for (int i = 0; i < IA::kLoads; ++i) {
       bool ok;
@@ -502,7 +558,6 @@ __device__ __forceinline__ void gemm_wave(const GemmArgs& g, int wave, int lane,
   const int jl = KS ? g.nks - 1 : 0;
   const float sp = g.act_scales[2 * jl];
   const float sn = g.act_scales[2 * jl + 1];
-  const float* const w_scales_last = g.w_scales + (int64_t)jl * g.Nout;
   const int i16 = lane & 15;
   const int rsub = (lane >> 4) * 4;
   // Input branches: the fp32 sum of the finished branches' epilogue parts
@@ -694,14 +749,12 @@ __device__ __forceinline__ void gemm_wave(const GemmArgs& g, int wave, int lane,
     coords(ti, m0, n0);
     float sw[NBW];
     unsigned coff[NBW];  // byte offset of this lane's column in a row, or out of range
+    lds_read_stride16<NBW>(sring + (ti % kScaleRing) * 256 + 16 * J0 + i16, sw);
 #pragma unroll
     for (int jj = 0; jj < NBW; ++jj) {
       const int col = n0 + 16 * (J0 + jj) + i16;
-      sw[jj] = w_scales_last[min(col, g.N - 1)];
       coff[jj] = col < g.N ? 4u * (unsigned)col : kOOB;
     }
-#pragma unroll
-    for (int jj = 0; jj < NBW; ++jj) asm volatile("" ::"v"(sw[jj]));
     auto yout = [&](int fi, int jj, int r) __attribute__((always_inline)) {
       int ap, an;
       accs(fi, jj, r, ap, an);
@@ -870,17 +923,19 @@ __global__ __launch_bounds__(kThreads, 1) void k2_gemm(GemmArgs g) {
   __shared__ __attribute__((aligned(16))) uint8_t st2[Lay::kStage];
   __shared__ __attribute__((aligned(16))) uint8_t st3[Lay::kStage];
   static_assert(kStages == 4, "one LDS object per stage");
+  // weight-scale ring of the plain tiles (single-Hadamard tiles use all of LDS)
+  __shared__ __attribute__((aligned(16))) float sring[(HS || KS) ? 4 : kScaleRing * 256];
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // uniform
   // waves w < NB - 8 also move weight pair w + 8; with NB <= 12 those are
   // all column-group-0 waves
   static_assert(NB >= 8 && NB <= 12, "wave roles");
   if (wave < NB - 8)
-    gemm_wave<A4, SYM, CFG, HS, KS, NB, 0, true>(g, wave, lane, st0, st1, st2, st3);
+    gemm_wave<A4, SYM, CFG, HS, KS, NB, 0, true>(g, wave, lane, st0, st1, st2, st3, sring);
   else if (wave < 4)
-    gemm_wave<A4, SYM, CFG, HS, KS, NB, 0, false>(g, wave, lane, st0, st1, st2, st3);
+    gemm_wave<A4, SYM, CFG, HS, KS, NB, 0, false>(g, wave, lane, st0, st1, st2, st3, sring);
   else
-    gemm_wave<A4, SYM, CFG, HS, KS, NB, 1, false>(g, wave, lane, st0, st1, st2, st3);
+    gemm_wave<A4, SYM, CFG, HS, KS, NB, 1, false>(g, wave, lane, st0, st1, st2, st3, sring);
 }
 
 // Compute units per device, queried on the first launch there. The grid
