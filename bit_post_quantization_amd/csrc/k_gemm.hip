@@ -268,6 +268,7 @@ __device__ __forceinline__ void wait_lgkm0() {
 constexpr int kSchedValu = 0x002;
 constexpr int kSchedMfma = 0x008;
 constexpr int kSchedDsRead = 0x100;
+constexpr int kSchedDsWrite = 0x200;
 
 // Issue order of one step's straight-line body: the activation-fragment
 // groups (half h, pair fi) each run their NBW MFMAs on the full codes, with
@@ -292,24 +293,30 @@ __device__ __forceinline__ void sched_mfmas() {
   }
 }
 
-template <int GR, int NBW, int NREADS, int VPER, bool DUAL>
+template <int GR, int NBW, int NREADS, int VPER, int VPER2, bool DUAL>
 __device__ __forceinline__ void sched_groups() {
   if constexpr (GR < 4) {
     constexpr int nr = NREADS * (GR + 1) / 4 - NREADS * GR / 4;
     if constexpr (DUAL) {
       sched_mfmas<0, NBW, VPER, 0>();
-      sched_mfmas<0, NBW, 0, nr>();
+      sched_mfmas<0, NBW, VPER2, nr>();
     } else {
       sched_mfmas<0, NBW, VPER, nr>();
     }
     sched_group<kSchedDsRead, (nr > NBW ? nr - NBW : 0)>();
-    sched_groups<GR + 1, NBW, NREADS, VPER, DUAL>();
+    sched_groups<GR + 1, NBW, NREADS, VPER, VPER2, DUAL>();
   }
 }
 
-template <int NBW, int NREADS, int VALU_PER_GROUP, bool DUAL>
+// VALU2_PER_GROUP: further VALU work slotted between the non-negative-plane
+// MFMAs (the weight transform of a later step); NWRITES LDS writes close the
+// step.
+template <int NBW, int NREADS, int VALU_PER_GROUP, bool DUAL, int VALU2_PER_GROUP = 0,
+          int NWRITES = 0>
 __device__ __forceinline__ void schedule_step() {
-  sched_groups<0, NBW, NREADS, (VALU_PER_GROUP + NBW - 1) / NBW, DUAL>();
+  sched_groups<0, NBW, NREADS, (VALU_PER_GROUP + NBW - 1) / NBW,
+               (VALU2_PER_GROUP + NBW - 1) / NBW, DUAL>();
+  sched_group<kSchedDsWrite, NWRITES>();
 }
 
 // n (4, 5 or 6) floats at p, p + 16, ... (LDS), read in one asm block that
@@ -358,7 +365,7 @@ constexpr int kScaleRing = 8;
 // pair w + 8, so a step's body has no branches and every step issues the
 // same number of loads: the compiler can then prove from the explicit
 // waits below that each LDS read finds its data landed.
-template <bool A4, bool SYM, bool CFG, bool HS, bool KS, int NB, int CG, bool TW>
+template <bool A4, bool SYM, bool CFG, bool HS, bool KS, int NB, int CG, bool TW, bool MK>
 __device__ __forceinline__ void gemm_wave(const GemmArgs& g, int wave, int lane, uint8_t* st0,
                                           uint8_t* st1, uint8_t* st2, uint8_t* st3,
                                           float* sring) {
@@ -492,6 +499,35 @@ __device__ __forceinline__ void gemm_wave(const GemmArgs& g, int wave, int lane,
     wait_vmcnt<n * (TW ? Lay::kOpsLow : Lay::kOpsHigh)>();
   };
 
+  // TASQ weight depth (MK): the weight bytes this wave's DMA brought into a
+  // slot (16 per lane per DMA instruction), read back by the lane that
+  // loaded them, magnitude-masked in place (trunc_mag4) and published by the
+  // next step barrier; each weight byte is masked once per workgroup. The
+  // masked step is two steps ahead of the MFMAs (its loads are waited for
+  // one step earlier than without the mask), so no extra barrier is needed.
+  // (Splitting the wave that also moves pair 8's share over the other SIMDs
+  // measured 1-1.5 % slower.)
+  constexpr int kTUnits = MK ? (TW ? 2 : 1) * IW::kLoads : 0;
+  uint32_t mlut = 0, mkeep = 0xFFFFFFFFu;
+  if constexpr (MK) {
+    const int kk = g.w_lsb_k;
+    mlut = ((1u << kk) - 1u) << 8;
+    mkeep = 0x01010101u * (0xFFu & ~((1u << kk) - 1u));
+  }
+  // Unit t: DMA instruction t % 2 of weight pair wave + 8 (t / 2).
+  auto mask_unit = [&](uint8_t* slot, int t) __attribute__((always_inline)) {
+    const int q = t / IW::kLoads, i = t % IW::kLoads;
+    v4u* p = reinterpret_cast<v4u*>(slot + Lay::kABytes + (wave + 8 * q) * IW::kBytes + i * 1024 +
+                                    lane * 16);
+    const v4u v = *p;
+    *p = v4u{trunc_mag4(v.x, mlut, mkeep), trunc_mag4(v.y, mlut, mkeep),
+             trunc_mag4(v.z, mlut, mkeep), trunc_mag4(v.w, mlut, mkeep)};
+  };
+  auto mask_slot = [&](uint8_t* slot) __attribute__((always_inline)) {
+#pragma unroll
+    for (int t = 0; t < kTUnits; ++t) mask_unit(slot, t);
+  };
+
   int roff_a[2], roff_w[2];
 #pragma unroll
   for (int h = 0; h < 2; ++h) {
@@ -529,7 +565,9 @@ __device__ __forceinline__ void gemm_wave(const GemmArgs& g, int wave, int lane,
 
   // Step s's MFMAs on `f` plus the reads of step s+1's fragments into `n`,
   // issued in the interleaved order of schedule_step.
-  auto compute = [&](const Frags& f, Frags& n, const uint8_t* nslot) __attribute__((always_inline)) {
+  auto compute = [&](const Frags& f, Frags& n, const uint8_t* nslot,
+                     uint8_t* tslot) __attribute__((always_inline)) {
+    mask_slot(tslot);
     read_all(n, nslot);
     v4i b[NBW][2];
 #pragma unroll
@@ -549,9 +587,9 @@ __device__ __forceinline__ void gemm_wave(const GemmArgs& g, int wave, int lane,
           for (int jj = 0; jj < NBW; ++jj) acc[0][fi][jj] = mfma(ap, b[jj][h], acc[0][fi][jj]);
         }
       }
-    constexpr int kReads = 4 + 2 * NBW;
+    constexpr int kReads = 4 + 2 * NBW + kTUnits;
     constexpr int kValu = (SYM ? 0 : 12) + (A4 ? 10 : 0);
-    schedule_step<NBW, kReads, kValu, !SYM>();
+    schedule_step<NBW, kReads, kValu, !SYM, (20 * kTUnits + 3) / 4, kTUnits>();
   };
 
   // Scales of the last input branch (the only one without input branches).
@@ -854,12 +892,13 @@ __device__ __forceinline__ void gemm_wave(const GemmArgs& g, int wave, int lane,
   // constant at every call site.
   auto step = [&](int s, auto uc) __attribute__((always_inline)) {
     constexpr int u = decltype(uc)::value;
-    wait_steps(IC<2>{});
+    wait_steps(IC<MK ? 1 : 2>{});
     wait_lgkm0();
     __builtin_amdgcn_s_barrier();
     issue(slots[u]);
-    // (on the last step this reads a stale slot; the values are never used)
-    compute(F[u & 1], F[(u + 1) & 1], slots[(u + 1) % kStages]);
+    // (on the last step this reads a stale slot; the values are never used;
+    // the masked slot holds step s+2, issued like every step)
+    compute(F[u & 1], F[(u + 1) & 1], slots[(u + 1) % kStages], slots[(u + 2) % kStages]);
     return ++cmp_k == nk;
   };
 
@@ -869,7 +908,14 @@ __device__ __forceinline__ void gemm_wave(const GemmArgs& g, int wave, int lane,
   issue(slots[1]);
   issue(slots[2]);
   issue(slots[3]);
-  wait_steps(IC<3>{});
+  if constexpr (MK) {
+    wait_steps(IC<2>{});  // steps 0 and 1 landed: mask this wave's bytes of them
+    mask_slot(slots[0]);
+    mask_slot(slots[1]);
+    wait_lgkm0();
+  } else {
+    wait_steps(IC<3>{});
+  }
   __builtin_amdgcn_s_barrier();
   read_all(F[0], slots[0]);
   zero_acc();
@@ -913,7 +959,7 @@ __device__ __forceinline__ void gemm_wave(const GemmArgs& g, int wave, int lane,
   if (sb + 2 < total) step_epi(sb + 2, IC<2>{});
 }
 
-template <bool A4, bool SYM, bool CFG, bool HS, bool KS, int NB>
+template <bool A4, bool SYM, bool CFG, bool HS, bool KS, int NB, bool MK>
 __global__ __launch_bounds__(kThreads, 1) void k2_gemm(GemmArgs g) {
   using Lay = Layout<A4, NB>;
   // One LDS object per ring stage: the compiler tracks DMA -> LDS writes per
@@ -931,11 +977,11 @@ __global__ __launch_bounds__(kThreads, 1) void k2_gemm(GemmArgs g) {
   // all column-group-0 waves
   static_assert(NB >= 8 && NB <= 12, "wave roles");
   if (wave < NB - 8)
-    gemm_wave<A4, SYM, CFG, HS, KS, NB, 0, true>(g, wave, lane, st0, st1, st2, st3, sring);
+    gemm_wave<A4, SYM, CFG, HS, KS, NB, 0, true, MK>(g, wave, lane, st0, st1, st2, st3, sring);
   else if (wave < 4)
-    gemm_wave<A4, SYM, CFG, HS, KS, NB, 0, false>(g, wave, lane, st0, st1, st2, st3, sring);
+    gemm_wave<A4, SYM, CFG, HS, KS, NB, 0, false, MK>(g, wave, lane, st0, st1, st2, st3, sring);
   else
-    gemm_wave<A4, SYM, CFG, HS, KS, NB, 1, false>(g, wave, lane, st0, st1, st2, st3, sring);
+    gemm_wave<A4, SYM, CFG, HS, KS, NB, 1, false, MK>(g, wave, lane, st0, st1, st2, st3, sring);
 }
 
 // Compute units per device, queried on the first launch there. The grid
@@ -958,7 +1004,7 @@ hipError_t device_cus(int& cus) {
   return e;
 }
 
-template <bool A4, bool SYM, bool CFG, bool HS, bool KS, int NB>
+template <bool A4, bool SYM, bool CFG, bool HS, bool KS, int NB, bool MK = false>
 hipError_t run(const GemmArgs& g, hipStream_t s) {
   const int rpt = CFG ? 64 : 128;
   const int T = (((CFG ? g.Mh : g.M) + rpt - 1) / rpt) * ((g.N + 16 * NB - 1) / (16 * NB));
@@ -966,7 +1012,7 @@ hipError_t run(const GemmArgs& g, hipStream_t s) {
   const hipError_t e = device_cus(cus);
   if (e != hipSuccess) return e;
   const int G = T < cus ? T : cus;
-  hipLaunchKernelGGL((k2_gemm<A4, SYM, CFG, HS, KS, NB>), dim3(G), dim3(kThreads), 0, s, g);
+  hipLaunchKernelGGL((k2_gemm<A4, SYM, CFG, HS, KS, NB, MK>), dim3(G), dim3(kThreads), 0, s, g);
   return hipGetLastError();
 }
 
@@ -1013,7 +1059,8 @@ hipError_t run_mode(const GemmArgs& g, int sym, int cfg, int hs, hipStream_t s) 
   // (the DiT-XL/2 W8A8 layers): this kernel measured 2-6 % faster than
   // k_gemm1.hip there. Every other plan runs k_gemm1.hip.
   if (!A4 && !sym && cfg && g.nks == 1 && g.N % 144 == 0)
-    return run<false, false, true, false, false, 9>(g, s);
+    return g.w_lsb_k > 0 ? run<false, false, true, false, false, 9, true>(g, s)
+                         : run<false, false, true, false, false, 9>(g, s);
   return hipErrorInvalidValue;
 }
 

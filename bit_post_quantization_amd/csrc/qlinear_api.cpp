@@ -595,14 +595,16 @@ ql_status qlinear_gemm(qlinear_plan_t p, const void* codes, const float* act_sca
     const int steps = j < p->nks ? (p->kseg[j + 1] - p->kseg[j] + 127) / 128 : 0;
     g.ksteps[j] = (steps + 2) / 3 * 3;
   }
-  g.w_lsb_k = p->w_lsb_k;
+  // Plans that keep a truncated copy hand the GEMM depth 0 (the copy is
+  // already truncated).
+  g.w_lsb_k = p->depth_in_gemm ? p->w_lsb_k : 0;
   const int a4 = p->d.a_bits == 4, sym = p->d.a_scale_mode == QL_ASCALE_SYMMETRIC;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   // Kernel choice: k_gemm.hip for single-Hadamard and 3-4-branch plans, and
-  // for plain int8 W8A8 DualScale CFG layers with 144-column tiles (measured
-  // faster there); k_gemm1.hip for everything else.
-  const bool plain_w8a8_cfg = p->depth_in_gemm && !p->packed4 && p->w_lsb_k == 0 &&
-                              p->nks == 1 && !a4 && !sym && cfg && g.N % 144 == 0;
+  // for int8 W8A8 DualScale CFG layers with 144-column tiles, at any TASQ
+  // depth (measured faster there); k_gemm1.hip for everything else.
+  const bool plain_w8a8_cfg = p->depth_in_gemm && !p->packed4 && p->nks == 1 && !a4 && !sym &&
+                              cfg && g.N % 144 == 0;
   const hipError_t e = p->depth_in_gemm && !plain_w8a8_cfg
                            ? ql::launch_gemm1(g, a4, sym, cfg, p->packed4, s)
                            : ql::launch_gemm(g, a4, sym, cfg, p->d.single_hadamard, s);

@@ -403,6 +403,18 @@ def test_input_branches_with_output_segments(torch, w_scale, seg, a_bits, x_dtyp
                x_dtype=x_dtype, w_scale=w_scale, seg=seg, tag=f"kseg+{w_scale}")
 
 
+@pytest.mark.parametrize("M,K,N,wk", [
+    (130, 528, 288, 1), (130, 528, 288, 4), (130, 528, 288, 7), (20480, 256, 288, 3)])
+def test_weight_lsb_view_wide_tiles(torch, M, K, N, wk):
+    # int8 W8A8 DualScale with CFG and 144-column tiles: the 8-wave GEMM masks
+    # the view's depth in LDS. Ragged rows and K; the large case streams one
+    # or two tiles per workgroup.
+    X = synth.gelu_normal(23, f"wlsbw/{M}/{K}/{wk}", M, K)
+    W = synth.weight_normal(23, f"wlsbw/W{M}/{K}/{wk}", N, K)
+    rows = None if M <= 1024 else sample_rows(M, True, 48, seed=wk)
+    check_layer(torch, X, W, M=M, K=K, N=N, cfg=1, w_lsb_k=wk, rows=rows, tag=f"wlsbw{wk}")
+
+
 def test_input_branches_static_lsb_view(torch):
     M, K, N, offs = 96, 768, 64, [0, 512, 768]
     X = np.concatenate([synth.silu_normal(42, "kseg/st/0", M, 512),
