@@ -1,6 +1,6 @@
 // K2 for HQ-DM's single Hadamard (hi/lo weight planes), SegLinear inputs of
 // 3 or 4 branches, and the W8A8 DualScale CFG layers with 144-column tiles
-// (where it measured faster than k_gemm1.hip). Integer
+// at any TASQ weight depth (where it measured faster than k_gemm1.hip). Integer
 // GEMM of the activation codes against the weight codes on the int8 matrix
 // cores of gfx950, both DualScale polarity planes in one kernel, with the
 // fp32 epilogue (scales, Hadamard normalisation, CFG combine) fused.
@@ -49,6 +49,10 @@
 //    combines each pair exactly in fp64 (epilogue_hs). Its tiles are 128 or
 //    192 weight rows (NB = 8 or 12; 192 uses all 160 KB of LDS with 8-bit
 //    activations).
+//  * TASQ weight depth (TASQ explainer 2: one stored buffer, low magnitude
+//    bits dropped per stage and layer): the stored codes reach LDS by DMA and
+//    each wave masks the 16-byte units its own DMA brought in, in place, two
+//    steps ahead of the MFMAs; the step barrier publishes them.
 //  * Input branches (SegQuant explainer 2.A, input segmentation): when the
 //    K loop crosses a branch end, the branch's epilogue part is folded into
 //    fp32 partial sums held in a per-thread workspace slice and the
