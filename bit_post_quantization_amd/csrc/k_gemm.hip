@@ -212,11 +212,6 @@ __device__ __forceinline__ float epi_part(int accp, int accn, float sp, float sn
   }
 }
 
-template <bool SYM>
-__device__ __forceinline__ float epi(int accp, int accn, float sp, float sn, float sw, float inv_b) {
-  return __fmul_rn(epi_part<SYM>(accp, accn, sp, sn, sw), inv_b);
-}
-
 // Tiles of workgroup b. When grid and tile counts divide by 8, each XCD
 // (workgroup id mod 8) owns a band of consecutive tiles. When that band is
 // R whole tile rows and its per_x workgroups divide into R rows of C
@@ -800,7 +795,9 @@ __device__ __forceinline__ void gemm_wave(const GemmArgs& g, int wave, int lane,
     auto yout = [&](int fi, int jj, int r) __attribute__((always_inline)) {
       int ap, an;
       accs(fi, jj, r, ap, an);
-      return epi<SYM>(ap, an, sp, sn, sw[jj], g.inv_b);
+      // plain tiles carry no rotation: the launcher admits them with
+      // 1/B = 1 only, so the exact multiply by 1/B is left out
+      return epi_part<SYM>(ap, an, sp, sn, sw[jj]);
     };
     const int rows_here = min(RPT, (CFG ? g.Mh : g.M) - m0);
     const __amdgpu_buffer_rsrc_t ry =
@@ -1059,10 +1056,11 @@ hipError_t run_mode(const GemmArgs& g, int sym, int cfg, int hs, hipStream_t s) 
     return cfg ? run<A4, false, true, false, true, 8>(g, s)
                : run<A4, false, false, false, true, 8>(g, s);
   }
-  // Plain int8 weights, 8-bit DualScale activations, CFG, 144-column tiles
-  // (the DiT-XL/2 W8A8 layers): this kernel measured 2-6 % faster than
-  // k_gemm1.hip there. Every other plan runs k_gemm1.hip.
-  if (!A4 && !sym && cfg && g.nks == 1 && g.N % 144 == 0)
+  // int8 weights at any TASQ depth, 8-bit DualScale activations, CFG,
+  // 144-column tiles, no rotation (the DiT-XL/2 W8A8 layers): this kernel
+  // measured 2-6 % faster than k_gemm1.hip there. Every other plan runs
+  // k_gemm1.hip.
+  if (!A4 && !sym && cfg && g.nks == 1 && g.N % 144 == 0 && g.inv_b == 1.0f)
     return g.w_lsb_k > 0 ? run<false, false, true, false, false, 9, true>(g, s)
                          : run<false, false, true, false, false, 9>(g, s);
   return hipErrorInvalidValue;

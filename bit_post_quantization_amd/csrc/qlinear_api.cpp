@@ -601,10 +601,11 @@ ql_status qlinear_gemm(qlinear_plan_t p, const void* codes, const float* act_sca
   const int a4 = p->d.a_bits == 4, sym = p->d.a_scale_mode == QL_ASCALE_SYMMETRIC;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   // Kernel choice: k_gemm.hip for single-Hadamard and 3-4-branch plans, and
-  // for int8 W8A8 DualScale CFG layers with 144-column tiles, at any TASQ
-  // depth (measured faster there); k_gemm1.hip for everything else.
+  // for int8 W8A8 DualScale CFG layers with 144-column tiles and no rotation,
+  // at any TASQ depth (measured faster there); k_gemm1.hip for everything
+  // else.
   const bool plain_w8a8_cfg = p->depth_in_gemm && !p->packed4 && p->nks == 1 && !a4 && !sym &&
-                              cfg && g.N % 144 == 0;
+                              cfg && g.N % 144 == 0 && p->d.hadamard_block == 0;
   const hipError_t e = p->depth_in_gemm && !plain_w8a8_cfg
                            ? ql::launch_gemm1(g, a4, sym, cfg, p->packed4, s)
                            : ql::launch_gemm(g, a4, sym, cfg, p->d.single_hadamard, s);
