@@ -479,13 +479,17 @@ def test_segments(torch, w_scale, seg):
 
 
 @pytest.mark.parametrize("a_bits", [8, 4])
-def test_codes_at_rounding_boundaries(torch, a_bits):
+@pytest.mark.parametrize("mx,mn", [(100.0, 50.0), (3.7, 91.3), (0.0123, 0.777), (1234.5, 0.5)])
+def test_codes_at_rounding_boundaries(torch, a_bits, mx, mn):
     """Values whose quotient by the scale lies on, or within a few ulps of, a
     half-integer: the cases where a product with the reciprocal scale could
-    round differently from the IEEE quotient. Codes must match exactly."""
+    round differently from the IEEE quotient, including quotients that the
+    float division rounds onto a half-integer (then rounded half to even)
+    although the exact quotient is not one. Codes must match exactly."""
+    from fractions import Fraction
     from bit_post_quantization_amd import QuantLinear
     qa = 127 if a_bits == 8 else 7
-    mx, mn = np.float32(100.0), np.float32(50.0)
+    mx, mn = np.float32(mx), np.float32(mn)
     sp, sn = mx / np.float32(qa), mn / np.float32(qa)
     vals = []
     for k in range(qa + 1):
@@ -499,9 +503,19 @@ def test_codes_at_rounding_boundaries(torch, a_bits):
                 vals.append(v)
     vals = np.asarray(vals, np.float32)
     vals = vals[(vals <= mx) & (vals >= -mn)]
+    # the set holds double-rounding cases: fl(v / s) on a half-integer, v / s not
+    ties = 0
+    for v in vals:
+        s_ = sp if v >= 0 else sn
+        fq = np.float32(v) / s_
+        if fq - np.floor(fq) == 0.5 and Fraction(float(v)) / Fraction(float(s_)) != Fraction(float(fq)):
+            ties += 1
+    assert ties > 0
     K = 256
     M = 2 * ((vals.size + K - 1) // K + 1)
-    X = synth.random_int_codes(3, "bnd/X", (M, K), -40, 40).astype(np.float32) * np.float32(0.5)
+    # filler strictly inside [-mn, mx], so that mx and -mn set the scales
+    X = (synth.random_int_codes(3, "bnd/X", (M, K), -40, 40).astype(np.float32)
+         * np.float32(min(mx, mn) / 64))
     flat = X.reshape(-1)
     flat[: vals.size] = vals
     flat[-1], flat[-2] = mx, -mn
