@@ -364,7 +364,7 @@ constexpr int kScaleRing = 8;
 // pair w + 8, so a step's body has no branches and every step issues the
 // same number of loads: the compiler can then prove from the explicit
 // waits below that each LDS read finds its data landed.
-template <bool A4, bool SYM, bool CFG, bool HS, bool KS, int NB, int CG, bool TW, bool MK>
+template <bool A4, bool SYM, bool CFG, bool HS, bool KS, int NB, int CG, bool TW, bool MK, bool DBG>
 __device__ __forceinline__ void gemm_wave(const GemmArgs& g, int wave, int lane, uint8_t* st0,
                                           uint8_t* st1, uint8_t* st2, uint8_t* st3,
                                           float* sring) {
@@ -700,7 +700,9 @@ __device__ __forceinline__ void gemm_wave(const GemmArgs& g, int wave, int lane,
         }
       asm volatile("" ::: "memory");
     }
-    if (g.dbg) dump_acc(m0, coff, j);
+    if constexpr (DBG) {
+      if (g.dbg) dump_acc(m0, coff, j);
+    }
     wait_vmcnt<0>();
   };
 
@@ -960,7 +962,7 @@ __device__ __forceinline__ void gemm_wave(const GemmArgs& g, int wave, int lane,
   if (sb + 2 < total) step_epi(sb + 2, IC<2>{});
 }
 
-template <bool A4, bool SYM, bool CFG, bool HS, bool KS, int NB, bool MK>
+template <bool A4, bool SYM, bool CFG, bool HS, bool KS, int NB, bool MK, bool DBG>
 __global__ __launch_bounds__(kThreads, 1) void k2_gemm(GemmArgs g) {
   using Lay = Layout<A4, NB>;
   // One LDS object per ring stage: the compiler tracks DMA -> LDS writes per
@@ -978,11 +980,11 @@ __global__ __launch_bounds__(kThreads, 1) void k2_gemm(GemmArgs g) {
   // all column-group-0 waves
   static_assert(NB >= 8 && NB <= 12, "wave roles");
   if (wave < NB - 8)
-    gemm_wave<A4, SYM, CFG, HS, KS, NB, 0, true, MK>(g, wave, lane, st0, st1, st2, st3, sring);
+    gemm_wave<A4, SYM, CFG, HS, KS, NB, 0, true, MK, DBG>(g, wave, lane, st0, st1, st2, st3, sring);
   else if (wave < 4)
-    gemm_wave<A4, SYM, CFG, HS, KS, NB, 0, false, MK>(g, wave, lane, st0, st1, st2, st3, sring);
+    gemm_wave<A4, SYM, CFG, HS, KS, NB, 0, false, MK, DBG>(g, wave, lane, st0, st1, st2, st3, sring);
   else
-    gemm_wave<A4, SYM, CFG, HS, KS, NB, 1, false, MK>(g, wave, lane, st0, st1, st2, st3, sring);
+    gemm_wave<A4, SYM, CFG, HS, KS, NB, 1, false, MK, DBG>(g, wave, lane, st0, st1, st2, st3, sring);
 }
 
 // Compute units per device, queried on the first launch there. The grid
@@ -1005,7 +1007,7 @@ hipError_t device_cus(int& cus) {
   return e;
 }
 
-template <bool A4, bool SYM, bool CFG, bool HS, bool KS, int NB, bool MK = false>
+template <bool A4, bool SYM, bool CFG, bool HS, bool KS, int NB, bool MK = false, bool DBG = false>
 hipError_t run(const GemmArgs& g, hipStream_t s) {
   const int rpt = CFG ? 64 : 128;
   const int T = (((CFG ? g.Mh : g.M) + rpt - 1) / rpt) * ((g.N + 16 * NB - 1) / (16 * NB));
@@ -1013,7 +1015,7 @@ hipError_t run(const GemmArgs& g, hipStream_t s) {
   const hipError_t e = device_cus(cus);
   if (e != hipSuccess) return e;
   const int G = T < cus ? T : cus;
-  hipLaunchKernelGGL((k2_gemm<A4, SYM, CFG, HS, KS, NB, MK>), dim3(G), dim3(kThreads), 0, s, g);
+  hipLaunchKernelGGL((k2_gemm<A4, SYM, CFG, HS, KS, NB, MK, DBG>), dim3(G), dim3(kThreads), 0, s, g);
   return hipGetLastError();
 }
 
@@ -1048,8 +1050,17 @@ hipError_t run_mode(const GemmArgs& g, int sym, int cfg, int hs, hipStream_t s) 
                : run<A4, true, false, true, false, 8>(g, s);
   }
   // Three or four input branches: 128-column tiles (the partial sums take
-  // 32 registers).
+  // 32 registers). The per-branch accumulator dump (a testing aid) lives in
+  // an instantiation of its own: its address arithmetic at every branch end
+  // would push the DualScale kernels past the register file (spills).
   if (g.nks > 2) {
+    if (g.dbg) {
+      if (sym)
+        return cfg ? run<A4, true, true, false, true, 8, false, true>(g, s)
+                   : run<A4, true, false, false, true, 8, false, true>(g, s);
+      return cfg ? run<A4, false, true, false, true, 8, false, true>(g, s)
+                 : run<A4, false, false, false, true, 8, false, true>(g, s);
+    }
     if (sym)
       return cfg ? run<A4, true, true, false, true, 8>(g, s)
                  : run<A4, true, false, false, true, 8>(g, s);

@@ -331,10 +331,11 @@ __global__ __launch_bounds__(kThreads) void k1_quantize(QuantArgs a) {
   }
 }
 
-// ---- One pass, for tensors that fit on chip (dynamic scales, no input
-// branches). One workgroup per compute unit holds its slice of X in
-// registers (up to kFUnits units per lane) and publishes its partial maxima;
-// workgroup 0 gathers them and publishes the tensor's maxima; every
+// ---- One pass, for tensors that fit on chip (dynamic scales, one or two
+// input branches). One workgroup per compute unit holds its slice of X in
+// registers (up to kFUnits units per lane) and publishes its partial maxima
+// (one pair per branch); workgroup 0 gathers them and publishes the
+// tensor's maxima; every
 // workgroup then quantizes from registers: X is read once (5 bytes per fp32
 // element moved in all, instead of 9). Every wait is bounded: a workgroup
 // that gives up (only possible if the grid was not all resident) scans X
@@ -391,8 +392,19 @@ __device__ __forceinline__ void block_max2(uint32_t& mp, uint32_t& mn, uint32_t 
   __syncthreads();
 }
 
-template <bool BF16, int HB, bool A4>
+// Column (in units) of unit g of the tensor, stepped lane-wise: each lane's
+// next unit lies kFThreads units further, and kFThreads % k_units < k_units,
+// so one conditional subtract keeps the column in range.
+__device__ __forceinline__ int step_col(int c, int step, int k_units) {
+  const int d = c + step;
+  return (uint32_t)(d - k_units) < (uint32_t)d ? d - k_units : d;
+}
+
+// NS: maxima pairs kept (1: the tensor's; 2: two input branches, whose
+// boundary ks_units[1] splits every row; a unit never straddles it).
+template <bool BF16, int HB, bool A4, int NS>
 __global__ __launch_bounds__(kFThreads, 1) void k1_fused(QuantArgs a, int U) {
+  static_assert(NS == 1 || NS == 2, "one or two maxima pairs");
   __shared__ uint32_t sm[2][kFWaves];
   const int tid = threadIdx.x, lane = tid & (kWave - 1);
   const int G = gridDim.x, b = blockIdx.x;
@@ -420,32 +432,69 @@ __global__ __launch_bounds__(kFThreads, 1) void k1_fused(QuantArgs a, int U) {
     for (int u = 0; u < kFUnits; ++u)
       if (u < U) fwht_block<HB>(e[u], lane);
   }
-  uint32_t mp = 0, mn = 0x80000000u;  // +0 and -0: zeros never win
+  // Branch tracking (NS = 2): column of this lane's first unit and the
+  // column step between its units; branch 1 starts at column kb1.
+  const int kun = a.k_units;
+  const int cstep = NS > 1 ? kFThreads % kun : 0;
+  const int col0 = NS > 1 ? (int)((first + tid) % kun) : 0;
+  const int kb1 = a.ks_units[1];
+  uint32_t mp[NS], mn[NS];
 #pragma unroll
-  for (int u = 0; u < kFUnits; ++u) max4(e[u], mp, mn);
-  mn &= 0x7FFFFFFFu;
-  block_max2(mp, mn, sm);
+  for (int j = 0; j < NS; ++j) {
+    mp[j] = 0;             // +0: zeros never win
+    mn[j] = 0x80000000u;   // -0
+  }
+  if constexpr (NS == 1) {
+#pragma unroll
+    for (int u = 0; u < kFUnits; ++u) max4(e[u], mp[0], mn[0]);
+  } else {
+    int col = col0;
+#pragma unroll
+    for (int u = 0; u < kFUnits; ++u) {
+      uint32_t up = 0, un = 0x80000000u;
+      max4(e[u], up, un);  // the unit's maxima, then its branch's
+      const bool b1 = col >= kb1;
+      mp[0] = b1 ? mp[0] : (uint32_t)max((int32_t)mp[0], (int32_t)up);
+      mn[0] = b1 ? mn[0] : max(mn[0], un);
+      mp[1] = b1 ? (uint32_t)max((int32_t)mp[1], (int32_t)up) : mp[1];
+      mn[1] = b1 ? max(mn[1], un) : mn[1];
+      col = step_col(col, cstep, kun);
+    }
+  }
+#pragma unroll
+  for (int j = 0; j < NS; ++j) {
+    mn[j] &= 0x7FFFFFFFu;
+    block_max2(mp[j], mn[j], sm);
+  }
 
   // Exchange: publish this workgroup's maxima; workgroup 0 gathers all of
-  // them and publishes the tensor's; the others wait for that.
+  // them and publishes the tensor's (per branch); the others wait for that.
   GridSync* gs = &a.ws->sync;
   const uint64_t tag = (uint64_t)a.seq << 32;
-  __shared__ uint32_t got[3];
+  __shared__ uint32_t got[1 + 2 * NS];
   if (tid == 0) {
-    __hip_atomic_store(&gs->word[0][b], tag | mp, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    __hip_atomic_store(&gs->word[1][b], tag | mn, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+#pragma unroll
+    for (int j = 0; j < NS; ++j) {
+      __hip_atomic_store(&gs->word[2 * j][b], tag | mp[j], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_store(&gs->word[2 * j + 1][b], tag | mn[j], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
   }
   bool ok = false;
-  uint32_t gp = 0, gn = 0;
+  uint32_t gp[NS], gn[NS];
+#pragma unroll
+  for (int j = 0; j < NS; ++j) gp[j] = gn[j] = 0;
   if (b == 0) {
     for (uint32_t it = 0; it < kFSpin; ++it) {
       bool mine = true;
       if (tid < G) {
-        const uint64_t w0 = __hip_atomic_load(&gs->word[0][tid], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        const uint64_t w1 = __hip_atomic_load(&gs->word[1][tid], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        mine = (w0 & ~0xFFFFFFFFull) == tag && (w1 & ~0xFFFFFFFFull) == tag;
-        gp = (uint32_t)w0;
-        gn = (uint32_t)w1;
+#pragma unroll
+        for (int j = 0; j < NS; ++j) {
+          const uint64_t w0 = __hip_atomic_load(&gs->word[2 * j][tid], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          const uint64_t w1 = __hip_atomic_load(&gs->word[2 * j + 1][tid], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          mine = mine && (w0 & ~0xFFFFFFFFull) == tag && (w1 & ~0xFFFFFFFFull) == tag;
+          gp[j] = (uint32_t)w0;
+          gn[j] = (uint32_t)w1;
+        }
       }
       if (__syncthreads_and(mine)) {
         ok = true;
@@ -457,12 +506,17 @@ __global__ __launch_bounds__(kFThreads, 1) void k1_fused(QuantArgs a, int U) {
     if (tid == 0) {
       got[0] = 0;
       for (uint32_t it = 0; it < kFSpin; ++it) {
-        const uint64_t r0 = __hip_atomic_load(&gs->result[0], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        const uint64_t r1 = __hip_atomic_load(&gs->result[1], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        if ((r0 & ~0xFFFFFFFFull) == tag && (r1 & ~0xFFFFFFFFull) == tag) {
+        uint64_t r[2 * NS];
+        bool all = true;
+#pragma unroll
+        for (int i = 0; i < 2 * NS; ++i) {
+          r[i] = __hip_atomic_load(&gs->result[i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          all = all && (r[i] & ~0xFFFFFFFFull) == tag;
+        }
+        if (all) {
           got[0] = 1;
-          got[1] = (uint32_t)r0;
-          got[2] = (uint32_t)r1;
+#pragma unroll
+          for (int i = 0; i < 2 * NS; ++i) got[1 + i] = (uint32_t)r[i];
           break;
         }
         __builtin_amdgcn_s_sleep(4);
@@ -471,54 +525,90 @@ __global__ __launch_bounds__(kFThreads, 1) void k1_fused(QuantArgs a, int U) {
     __syncthreads();
     ok = got[0] != 0;
     // every thread takes the tensor's maxima (the max below leaves them as they are)
-    gp = ok ? got[1] : 0;
-    gn = ok ? got[2] : 0;
+#pragma unroll
+    for (int j = 0; j < NS; ++j) {
+      gp[j] = ok ? got[1 + 2 * j] : 0;
+      gn[j] = ok ? got[2 + 2 * j] : 0;
+    }
   }
   if (!ok) {
     // Fallback: the maxima of the whole tensor, read here.
     if (tid == 0) __hip_atomic_fetch_add(&gs->fallbacks, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     const __amdgpu_buffer_rsrc_t rall = buffer_rsrc(a.X, (uint32_t)(a.nunits * kUnitBytes));
-    uint32_t fp = 0, fn = 0x80000000u;
+    uint32_t fp[NS], fn[NS];
+#pragma unroll
+    for (int j = 0; j < NS; ++j) {
+      fp[j] = 0;
+      fn[j] = 0x80000000u;
+    }
     for (int64_t i = tid; i < a.nunits; i += kFThreads) {
       float f[4];
       load_unit<BF16>(rall, (uint32_t)i * kUnitBytes, f);
       if constexpr (HB > 0) fwht_block<HB>(f, lane);
-      max4(f, fp, fn);
+      if constexpr (NS == 1) {
+        max4(f, fp[0], fn[0]);
+      } else {
+        const int j = (int)(i % kun) >= kb1 ? 1 : 0;
+        uint32_t up = 0, un = 0x80000000u;
+        max4(f, up, un);
+        fp[j] = (uint32_t)max((int32_t)fp[j], (int32_t)up);
+        fn[j] = max(fn[j], un);
+      }
     }
-    gp = fp;
-    gn = fn & 0x7FFFFFFFu;
+#pragma unroll
+    for (int j = 0; j < NS; ++j) {
+      gp[j] = fp[j];
+      gn[j] = fn[j] & 0x7FFFFFFFu;
+    }
   }
-  block_max2(gp, gn, sm);
-  if (b == 0 && tid == 0) {  // the tensor's maxima, for the other workgroups
-    __hip_atomic_store(&gs->result[0], tag | gp, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    __hip_atomic_store(&gs->result[1], tag | gn, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  float sps[NS], sns[NS], rps[NS], rns[NS];
+#pragma unroll
+  for (int j = 0; j < NS; ++j) {
+    block_max2(gp[j], gn[j], sm);
+    if (b == 0 && tid == 0) {  // the tensor's maxima, for the other workgroups
+      __hip_atomic_store(&gs->result[2 * j], tag | gp[j], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_store(&gs->result[2 * j + 1], tag | gn[j], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    const float mx = __uint_as_float(gp[j]), mnv = __uint_as_float(gn[j]);
+    float sp, sn;
+    if (a.sym) {
+      sp = (mx > mnv ? mx : mnv) / a.qa;
+      sn = sp;
+    } else {
+      sp = mx / a.qa;
+      sn = mnv / a.qa;
+    }
+    if (b == 0 && tid == 0) {
+      a.act_scales[2 * j] = sp;
+      a.act_scales[2 * j + 1] = sn;
+    }
+    sps[j] = sp;
+    sns[j] = sn;
+    rps[j] = sp > 0.0f ? 1.0f / sp : 0.0f;
+    rns[j] = sn > 0.0f ? 1.0f / sn : 0.0f;
   }
-  const float mx = __uint_as_float(gp), mnv = __uint_as_float(gn);
-  float sp, sn;
-  if (a.sym) {
-    sp = (mx > mnv ? mx : mnv) / a.qa;
-    sn = sp;
-  } else {
-    sp = mx / a.qa;
-    sn = mnv / a.qa;
-  }
-  if (b == 0 && tid == 0) {
-    a.act_scales[0] = sp;
-    a.act_scales[1] = sn;
-  }
-  const float rp = sp > 0.0f ? 1.0f / sp : 0.0f;
-  const float rn = sn > 0.0f ? 1.0f / sn : 0.0f;
   constexpr uint32_t kCodeBytes = A4 ? 2 : 4;
   const __amdgpu_buffer_rsrc_t rc =
       buffer_rsrc(reinterpret_cast<uint8_t*>(a.codes) + first * kCodeBytes, here * kCodeBytes);
   const LsbMask mk(a.keep_mask);
   auto quant_all = [&](auto symc) __attribute__((always_inline)) {
     constexpr bool SYM = decltype(symc)::value;
+    int col = col0;
 #pragma unroll
     for (int u = 0; u < kFUnits; ++u) {
-      if (u < U)
+      if (u < U) {
+        float sp = sps[0], sn = sns[0], rp = rps[0], rn = rns[0];
+        if constexpr (NS == 2) {
+          const bool b1 = col >= kb1;
+          sp = b1 ? sps[1] : sp;
+          sn = b1 ? sns[1] : sn;
+          rp = b1 ? rps[1] : rp;
+          rn = b1 ? rns[1] : rn;
+          col = step_col(col, cstep, kun);
+        }
         store_unit<A4>(rc, (uint32_t)(u * kFThreads + tid) * kCodeBytes,
                        quant_pack<SYM>(e[u], sp, sn, rp, rn, a.qa), mk);
+      }
     }
   };
   if (a.sym)
@@ -540,14 +630,14 @@ int balanced_grid(int nch, int cap) {
 }
 
 // One-pass launch when the tensor fits in the registers of one workgroup
-// per compute unit (and no branches, dynamic scales, HB 0 or 128): returns
-// false to let the caller run the two passes.
-template <bool BF16, int HB, bool A4>
+// per compute unit (dynamic scales, one or two input branches, HB 0 or 128):
+// returns false to let the caller run the two passes.
+template <bool BF16, int HB, bool A4, int NS>
 bool run_fused(const QuantArgs& a, hipStream_t s, hipError_t& e) {
   if constexpr (HB != 0 && HB != 128) {
     return false;
   } else {
-    if (a.static_scales || a.nks != 1 || a.nunits <= 0 || a.seq == 0) return false;
+    if (a.static_scales || a.nks != NS || a.nunits <= 0 || a.seq == 0) return false;
     int dev = 0, cus = 0;
     if (hipGetDevice(&dev) != hipSuccess ||
         hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
@@ -556,7 +646,7 @@ bool run_fused(const QuantArgs& a, hipStream_t s, hipError_t& e) {
     const int64_t U = (a.nunits + per - 1) / per;
     if (U > kFUnits || cus > kMaxReduceBlocks) return false;
     const int G = (int)((a.nunits + U * kFThreads - 1) / (U * kFThreads));
-    hipLaunchKernelGGL((k1_fused<BF16, HB, A4>), dim3(G), dim3(kFThreads), 0, s, a, (int)U);
+    hipLaunchKernelGGL((k1_fused<BF16, HB, A4, NS>), dim3(G), dim3(kFThreads), 0, s, a, (int)U);
     e = hipGetLastError();
     return true;
   }
@@ -564,9 +654,9 @@ bool run_fused(const QuantArgs& a, hipStream_t s, hipError_t& e) {
 
 template <bool BF16, int HB, bool A4, bool KS>
 hipError_t run_ks(QuantArgs a, hipStream_t s) {
-  if constexpr (!KS) {
+  {
     hipError_t e = hipSuccess;
-    if (run_fused<BF16, HB, A4>(a, s, e)) return e;
+    if (run_fused<BF16, HB, A4, KS ? 2 : 1>(a, s, e)) return e;
   }
   const int nch = chunks_of(a.nunits);
   const int g = balanced_grid(nch, kQuantBlocks);

@@ -12,19 +12,21 @@ namespace ql {
 constexpr int kMaxReduceBlocks = 1024;
 constexpr int kMaxKSeg = 4;  // input branches (SegLinear input segmentation)
 // Grid exchange of the one-pass quantizer. Workgroup b writes its partial
-// maxima as word[j][b] = (sequence number << 32) | bits (j = 0: max, 1: the
-// most negative value's magnitude); workgroup 0 waits for every word of the
-// grid to carry the call's number, folds them, and writes the maxima of the
-// tensor the same way into result[j], which the other workgroups wait for.
-// 64-bit words are written and read whole, so a tag and its value arrive
-// together and no fence is needed; nothing is reset between calls. Zero at
-// allocation (sequence numbers start at 1).
+// maxima of input branch j as word[2j][b] = (sequence number << 32) | bits
+// (the maximum) and word[2j+1][b] (the most negative value's magnitude);
+// workgroup 0 waits for every word of the grid to carry the call's number,
+// folds them, and writes the maxima of each branch the same way into
+// result[2j], result[2j+1], which the other workgroups wait for. 64-bit
+// words are written and read whole, so a tag and its value arrive together
+// and no fence is needed; nothing is reset between calls. Zero at allocation
+// (sequence numbers start at 1).
 struct GridSync {
-  uint64_t word[2][kMaxReduceBlocks];
-  uint64_t result[2];
+  uint64_t word[2 * kMaxKSeg][kMaxReduceBlocks];
+  uint64_t result[2 * kMaxKSeg];
   uint32_t fallbacks;  // workgroups that stopped waiting and scanned X themselves
-  uint32_t pad[59];
+  uint32_t pad[47];
 };
+static_assert(sizeof(GridSync) % 256 == 0, "exchange words keep their alignment");
 struct ReduceWs {
   // per branch: bits of max(+0, max x), max(+0, -min x)
   uint32_t part[kMaxKSeg][2][kMaxReduceBlocks];

@@ -210,7 +210,8 @@ ql_status enqueue_lsb(struct qlinear_plan* view, const struct qlinear_plan* base
 // Reduction workspace of qlinear_quantize_act_noalloc: one copy per device,
 // holding every partial maximum a call can write (kMaxKSeg branches x
 // kMaxReduceBlocks pairs, 32 KiB) and the one-pass quantizer's exchange
-// words (16 KiB; zero when the library is loaded). Host code never passes `scratch`
+// words (kMaxKSeg branches x 2 x kMaxReduceBlocks tagged 64-bit words,
+// 64.25 KiB; zero when the library is loaded). Host code never passes `scratch`
 // itself to a kernel (that name is a host-side stand-in): it passes the
 // device address looked up once per device below.
 static __device__ __align__(256) uint8_t scratch[sizeof(ql::ReduceWs)] = {};

@@ -230,7 +230,7 @@ ql_status qlinear_quantize_act(qlinear_plan_t p, const void* X, int32_t M, int32
  * capture, tight serving loops, harnesses that forbid hipMalloc): the same
  * computation, arguments, results and errors as qlinear_quantize_act, but
  * the per-block partial maxima of a dynamic-scale call go to a scratch array
- * that the library keeps in device memory (48.25 KiB per device, reserved when
+ * that the library keeps in device memory (96.25 KiB per device, reserved when
  * the library is loaded, held until the process ends) instead of the plan's
  * workspace. The scratch holds every partial a call writes (at most 1024 per
  * input branch, whatever M), so no size is refused for its sake; a call

@@ -565,6 +565,32 @@ def test_one_pass_quantizer_limits(torch, a_bits, B, x_dtype, lsb_k, a_scale):
         say(f"  codes: {st}")
         assert_codes(st)
 
+@pytest.mark.parametrize("K,offs,a_bits,B,x_dtype,lsb_k,a_scale", [
+    (1408, (0, 256, 1408), 8, 0, "f32", 0, "dual"),
+    (2304, (0, 1152, 2304), 4, 128, "bf16", 1, "dual"),
+    (4608, (0, 3456, 4608), 8, 128, "f32", 2, "symmetric")])
+def test_one_pass_quantizer_limits_two_branches(torch, K, offs, a_bits, B, x_dtype, lsb_k,
+                                                a_scale):
+    # Two input branches (SegQuant explainer 2.A) also run in one pass up to
+    # 40 units of 4 values per lane: each lane tracks its units' columns
+    # (K / 4 = 352 units per row makes the lane's column step 160, wrapping
+    # within rows), and the grid exchanges one maxima pair per branch. The
+    # largest such tensor and one row more (two passes) must both give the
+    # oracle's per-branch scales, codes, accumulators and outputs.
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    N = 16
+    M1 = (40 * cus * 512 * 4) // K
+    W = synth.weight_normal(45, f"onepass2/W/{K}", N, K)
+    for M in (M1, M1 + 1):
+        X = synth.silu_normal(45, f"onepass2/{M}/{K}", M, K)
+        if x_dtype == "bf16":
+            X = synth.f32_to_bf16_bits(X)
+        rows = np.arange(0, M, 61)
+        check_kseg(torch, X, W, M=M, K=K, N=N, offs=list(offs), a_bits=a_bits, w_bits=8, B=B,
+                   a_scale=a_scale, x_dtype=x_dtype, lsb_k=lsb_k, rows=rows,
+                   tag=f"one-pass limit M={M}")
+
+
 def test_static_scales(torch):
     M, K, N = 64, 256, 80
     X = synth.silu_normal(4, "static/X", M, K)
