@@ -202,12 +202,17 @@ __device__ __forceinline__ void scales_from_partials(const QuantArgs& a, int j, 
 
 // Codes of the four values of a unit, packed one per byte (element i in
 // byte i); the same codes as quant_dual (round half even of the correctly
-// rounded quotient v / s, clamped), computed from t = v * (1/s): the
-// quotient and t differ by less than |t| * 2^-22, so wherever t lies
-// farther than |t| * 2^-20 + 2^-20 from every half-integer both round to
-// the same integer. Units with a value closer than that (and non-finite t)
-// are redone with the division; that is rare and wave-uniform work is
-// skipped when no lane needs it. Rounding: m = t + 1.5 * 2^23 is t rounded
+// rounded quotient Q = fl(v / s), clamped), computed from t = fl(v * fl(1/s)).
+// With u = 2^-24: fl(1/s) and t each carry one relative rounding error of
+// at most u, and Q one more, so |t - Q| <= 3u|q|(1 + u) (q the exact
+// quotient), below |t| * 2^-22. The guard below computes
+// z = fl(|t| * 2^-22 + d), d = |t - rint(t)| exactly (Sterbenz), and takes
+// the product's integer when z < 0.5 - 2^-23; then the distance from t to
+// every half-integer, 0.5 - d, exceeds |t| * 2^-22 + 2^-24 > |t - Q|, so t
+// and Q lie strictly on one side of every half-integer and round alike
+// (a Q that rounds onto a half-integer is caught too). Units with a closer
+// value (and non-finite t, or |t| >= 2^21) are redone with the division;
+// that is rare and wave-uniform work is skipped when no lane needs it. Rounding: m = t + 1.5 * 2^23 is t rounded
 // half to even into the units of [2^23, 2^24) (the sum's even mantissas are
 // the even integers), so m - 1.5 * 2^23 = rint(t) for |t| < 2^22, and after
 // clamping m to 1.5 * 2^23 +- qa the code is the low byte of m's bits (the
@@ -226,8 +231,8 @@ __device__ __forceinline__ uint32_t quant_pack(const float (&e)[4], float sp, fl
     const float t = v * (SYM ? rp : (v >= 0.0f ? rp : rn));
     const float s = t + kMagic;
     const float r = s - kMagic;
-    const float z = fmaf(fabsf(t), 0x1p-20f, fabsf(t - r));
-    slow |= !(z < 0x1.fffcp-2f);  // 0.5 - 2^-19
+    const float z = fmaf(fabsf(t), 0x1p-22f, fabsf(t - r));
+    slow |= !(z < 0x1.fffff8p-2f);  // 0.5 - 2^-23
     m[i] = __builtin_amdgcn_fmed3f(s, kMagic - qa, kMagic + qa);
   }
   if (slow) {
@@ -254,10 +259,11 @@ struct LsbMask {
   }
 };
 
-template <bool A4>
+// LSB: truncation known at compile time (1: on, 0: off); -1: test mk.on.
+template <bool A4, int LSB = -1>
 __device__ __forceinline__ void store_unit(const __amdgpu_buffer_rsrc_t& rc, uint32_t off,
                                            uint32_t p, const LsbMask& mk) {
-  if (mk.on) p = trunc_mag4(p, mk.lut, mk.keep);
+  if (LSB == 1 || (LSB == -1 && mk.on)) p = trunc_mag4(p, mk.lut, mk.keep);
   if constexpr (A4) {
     const uint32_t q = p & 0x0F0F0F0Fu;
     const uint32_t r = q | (q >> 4);  // byte 0 = c0 | c1 << 4, byte 2 = c2 | c3 << 4
@@ -591,8 +597,9 @@ __global__ __launch_bounds__(kFThreads, 1) void k1_fused(QuantArgs a, int U) {
   const __amdgpu_buffer_rsrc_t rc =
       buffer_rsrc(reinterpret_cast<uint8_t*>(a.codes) + first * kCodeBytes, here * kCodeBytes);
   const LsbMask mk(a.keep_mask);
-  auto quant_all = [&](auto symc) __attribute__((always_inline)) {
+  auto quant_all = [&](auto symc, auto lsbc) __attribute__((always_inline)) {
     constexpr bool SYM = decltype(symc)::value;
+    constexpr int LSB = decltype(lsbc)::value ? 1 : 0;
     int col = col0;
 #pragma unroll
     for (int u = 0; u < kFUnits; ++u) {
@@ -606,15 +613,24 @@ __global__ __launch_bounds__(kFThreads, 1) void k1_fused(QuantArgs a, int U) {
           rn = b1 ? rns[1] : rn;
           col = step_col(col, cstep, kun);
         }
-        store_unit<A4>(rc, (uint32_t)(u * kFThreads + tid) * kCodeBytes,
-                       quant_pack<SYM>(e[u], sp, sn, rp, rn, a.qa), mk);
+        store_unit<A4, LSB>(rc, (uint32_t)(u * kFThreads + tid) * kCodeBytes,
+                            quant_pack<SYM>(e[u], sp, sn, rp, rn, a.qa), mk);
       }
     }
   };
-  if (a.sym)
-    quant_all(std::true_type{});
-  else
-    quant_all(std::false_type{});
+  // the scale mode and the truncation are uniform: one straight-line
+  // quantize phase per combination, no per-unit test
+  if (a.sym) {
+    if (mk.on)
+      quant_all(std::true_type{}, std::true_type{});
+    else
+      quant_all(std::true_type{}, std::false_type{});
+  } else {
+    if (mk.on)
+      quant_all(std::false_type{}, std::true_type{});
+    else
+      quant_all(std::false_type{}, std::false_type{});
+  }
 }
 
 int chunks_of(int64_t nunits) {

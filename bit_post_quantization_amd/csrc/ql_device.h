@@ -56,11 +56,22 @@ __device__ __forceinline__ void fwht_in_lane(float& e0, float& e1, float& e2, fl
   e3 = a1 - a3;
 }
 
+// Cross-lane stage h = 4L. The lower lane holds a (position j) and takes
+// a + b; the upper lane holds b (position j + h) and takes a - b. Both are
+// one fused multiply-add o + sg * e with sg = +1 or -1 per lane: sg * e is
+// exact, so the single rounding gives exactly the correctly rounded sum or
+// difference (signed zeros included), in one instruction instead of an add,
+// a subtract and a select.
 template <int L>  // lane distance L = h / 4
-__device__ __forceinline__ void fwht_cross_stage(float& e, bool upper) {
+__device__ __forceinline__ void fwht_cross_stage(float& e, float sg) {
   const float o = xor_lane<L>(e);
-  // lower lane holds a (position j), upper lane holds b (position j + h)
-  e = upper ? (o - e) : (e + o);
+  e = __builtin_fmaf(e, sg, o);
+}
+
+// Sign of the upper lanes of stage h = 4L.
+template <int L>
+__device__ __forceinline__ float fwht_sign(int lane) {
+  return (lane & L) ? -1.0f : 1.0f;
 }
 
 template <int B>
@@ -68,29 +79,29 @@ __device__ __forceinline__ void fwht_block(float (&e)[4], int lane) {
   static_assert(B >= 4 && B <= 128 && (B & (B - 1)) == 0, "block size");
   fwht_in_lane(e[0], e[1], e[2], e[3]);
   if constexpr (B >= 8) {
-    const bool up = lane & 1;
+    const float sg = fwht_sign<1>(lane);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) fwht_cross_stage<1>(e[i], up);
+    for (int i = 0; i < 4; ++i) fwht_cross_stage<1>(e[i], sg);
   }
   if constexpr (B >= 16) {
-    const bool up = lane & 2;
+    const float sg = fwht_sign<2>(lane);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) fwht_cross_stage<2>(e[i], up);
+    for (int i = 0; i < 4; ++i) fwht_cross_stage<2>(e[i], sg);
   }
   if constexpr (B >= 32) {
-    const bool up = lane & 4;
+    const float sg = fwht_sign<4>(lane);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) fwht_cross_stage<4>(e[i], up);
+    for (int i = 0; i < 4; ++i) fwht_cross_stage<4>(e[i], sg);
   }
   if constexpr (B >= 64) {
-    const bool up = lane & 8;
+    const float sg = fwht_sign<8>(lane);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) fwht_cross_stage<8>(e[i], up);
+    for (int i = 0; i < 4; ++i) fwht_cross_stage<8>(e[i], sg);
   }
   if constexpr (B >= 128) {
-    const bool up = lane & 16;
+    const float sg = fwht_sign<16>(lane);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) fwht_cross_stage<16>(e[i], up);
+    for (int i = 0; i < 4; ++i) fwht_cross_stage<16>(e[i], sg);
   }
 }
 
