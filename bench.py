@@ -284,6 +284,55 @@ def copy_calibration(torch):
     print(json.dumps({"copy_bytes": COPY_BYTES, "reps": COPY_REPS}), flush=True)
 
 
+PROBE_ITERS = 4000   # per probe launch: ~0.5 ms of MFMA work on every SIMD
+
+
+def measured_ceilings(torch):
+    """What the chip sustains, measured live beside the spec peaks: the int8
+    MFMA rate of the library's probe kernel (register operands, no memory,
+    no barrier; random operands, which switch the multiplier inputs on every
+    instruction as real codes do, and constant ones, which do not; the best
+    of one and two waves per SIMD) and the rate of a device-to-device copy
+    of 512 MiB (bytes read + written)."""
+    from bit_post_quantization_amd import qlinear_probe_mfma
+    cus = torch.cuda.get_device_properties(torch.cuda.current_device()).multi_processor_count
+    g = torch.Generator(device="cuda")
+    g.manual_seed(0)
+    ops = {"random": torch.randint(-128, 128, (16, 64, 16), dtype=torch.int8, device="cuda",
+                                   generator=g),
+           "constant": torch.full((16, 64, 16), 3, dtype=torch.int8, device="cuda")}
+    out = {}
+
+    def timed(fn, reps=5):
+        fn()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        a.record()
+        for _ in range(reps):
+            fn()
+        b.record()
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) * 1e-3 / reps
+
+    for name, o in ops.items():
+        best = 0.0
+        for wps in (1, 2):
+            sink = torch.empty(cus * 256 * wps, dtype=torch.int32, device="cuda")
+            t = timed(lambda: qlinear_probe_mfma(o, PROBE_ITERS, wps, sink))
+            best = max(best, cus * 4 * wps * PROBE_ITERS * 16 * 32768 / t / 1e12)
+        out[f"mfma_int8_{name}_operands_tops"] = round(best, 1)
+    src = torch.empty(COPY_BYTES, dtype=torch.uint8, device="cuda").fill_(1)
+    dst = torch.empty_like(src)
+    t = timed(lambda: dst.copy_(src))
+    out["hbm_copy_gbps"] = round(2 * COPY_BYTES / t / 1e9, 1)
+    out["method"] = ("int8 MFMA: qlinear_probe_mfma, %d iterations of 16 independent "
+                     "v_mfma_i32_16x16x64_i8 per wave, one workgroup per CU, best of 1 and 2 "
+                     "waves per SIMD; copy: torch copy_ of 512 MiB, read + written bytes"
+                     % PROBE_ITERS)
+    del src, dst
+    return out
+
+
 def gemm_source_hash():
     """SHA-256 of the GEMM source's code: comments and blank lines removed,
     so that editing a comment does not invalidate a profile."""
@@ -766,6 +815,14 @@ def main():
     }
     if args.workload in ("c4", "c4g"):
         out["bops"] = bops_report(Ls, wl.M)
+    # the kernels against what the chip sustains (measured here), beside
+    # their fractions of the spec peaks
+    ceil = measured_ceilings(torch)
+    out["ceilings"] = ceil
+    out["roofline"]["frac_of_measured_ceiling"] = round(
+        out["roofline"]["achieved"] / ceil["mfma_int8_random_operands_tops"], 4)
+    out["act_quant"]["frac_of_measured_copy"] = round(
+        out["act_quant"]["achieved"] / ceil["hbm_copy_gbps"], 4)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(layers, args.cpu_seconds)
     print(json.dumps(out), flush=True)

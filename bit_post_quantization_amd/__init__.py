@@ -11,5 +11,5 @@ from .qlinear import (  # noqa: F401
     Plan, QLError, QuantLinear, qlinear_cfg_combine, qlinear_gamp_allocate, qlinear_gemm,
     qlinear_plan,
     qlinear_plan_destroy, qlinear_plan_lsb_update, qlinear_plan_lsb_view, qlinear_plan_weights,
-    qlinear_quantize_act, qlinear_quantize_act_noalloc, qlinear_version,
+    qlinear_probe_mfma, qlinear_quantize_act, qlinear_quantize_act_noalloc, qlinear_version,
 )

@@ -12,7 +12,8 @@ OBJ = os.path.join(PKG, "_obj")
 LIB = os.path.join(PKG, "libqlinear.so")
 ARCH = "gfx950"
 
-SOURCES = ["k_quant.hip", "k_gemm.hip", "k_gemm1.hip", "k_misc.hip", "qlinear_api.cpp", "gamp.cpp"]
+SOURCES = ["k_quant.hip", "k_gemm.hip", "k_gemm1.hip", "k_misc.hip", "k_probe.hip",
+           "qlinear_api.cpp", "gamp.cpp"]
 
 # -ffp-contract=off: the epilogue's multiply-then-add order is part of the
 # numerics (no fused multiply-add). Correctly rounded fp32 division is the

@@ -22,7 +22,7 @@ EXPORTS = (
     "qlinear_plan", "qlinear_plan_destroy", "qlinear_plan_weights", "qlinear_quantize_act",
     "qlinear_gemm", "qlinear_cfg_combine", "qlinear_last_error", "qlinear_version",
     "qlinear_plan_lsb_view", "qlinear_plan_lsb_update", "qlinear_gamp_allocate",
-    "qlinear_quantize_act_noalloc",
+    "qlinear_quantize_act_noalloc", "qlinear_probe_mfma",
 )
 
 
@@ -68,6 +68,7 @@ def load() -> ctypes.CDLL:
         "qlinear_quantize_act_noalloc": ([P, P, I32, I32, P, P, P, P], ctypes.c_int),
         "qlinear_gemm": ([P, P, P, I32, I32, F32, P, P, P], ctypes.c_int),
         "qlinear_cfg_combine": ([P, I32, I32, F32, P, P], ctypes.c_int),
+        "qlinear_probe_mfma": ([P, I32, I32, P, P], ctypes.c_int),
         "qlinear_last_error": ([], ctypes.c_char_p),
         "qlinear_version": ([], ctypes.c_char_p),
     }

@@ -99,6 +99,11 @@ inline hipError_t launch_gemm1(const GemmArgs& g, int a4, int sym, int cfg, int 
   return sym ? launch_gemm1_a0_s1(g, cfg, w4, s) : launch_gemm1_a0_s0(g, cfg, w4, s);
 }
 
+// Measurement aid: the int8 MFMA ceiling microkernel (one workgroup of
+// 256 * waves_per_simd threads per block, blocks = compute units).
+hipError_t launch_probe_mfma(const void* ops, int iters, int waves_per_simd, int blocks, int* sink,
+                             hipStream_t s);
+
 // K3: standalone CFG combine.
 hipError_t launch_cfg_combine(const float* Y, int64_t half_elems, float w, float* out,
                               hipStream_t s);

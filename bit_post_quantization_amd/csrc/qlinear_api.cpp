@@ -614,6 +614,24 @@ ql_status qlinear_gemm(qlinear_plan_t p, const void* codes, const float* act_sca
   return ok();
 }
 
+ql_status qlinear_probe_mfma(const void* operands, int32_t iters, int32_t waves_per_simd,
+                             int32_t* sink, void* stream) {
+  if (!operands || !sink) return fail(QL_ERR_ARG, "operands or sink is NULL");
+  if (iters < 0 || iters > (1 << 24)) return fail(QL_ERR_ARG, "iters = %d must be in [0, 2^24]", iters);
+  if (waves_per_simd != 1 && waves_per_simd != 2)
+    return fail(QL_ERR_ARG, "waves_per_simd = %d must be 1 or 2", waves_per_simd);
+  if (!aligned(operands, 16) || !aligned(sink, 4))
+    return fail(QL_ERR_ARG, "operands must be 16-byte and sink 4-byte aligned");
+  int dev = 0, cus = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+  if (e != hipSuccess) return hip_fail(e, "querying the compute units");
+  e = ql::launch_probe_mfma(operands, iters, waves_per_simd, cus, sink,
+                            reinterpret_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "launching the MFMA probe");
+  return ok();
+}
+
 ql_status qlinear_cfg_combine(const float* Y, int32_t M, int32_t N, float w, float* out,
                               void* stream) {
   if (M < 0 || N < 1) return fail(QL_ERR_ARG, "M = %d, N = %d: need M >= 0, N >= 1", M, N);

@@ -131,6 +131,12 @@ def qlinear_cfg_combine(Y, M: int, N: int, w: float, out, stream=None) -> None:
     check(_lib.load().qlinear_cfg_combine(_ptr(Y), M, N, float(w), _ptr(out), _stream(stream)))
 
 
+def qlinear_probe_mfma(operands, iters: int, waves_per_simd: int, sink, stream=None) -> None:
+    """Measurement aid: the int8 MFMA ceiling microkernel (include/qlinear.h)."""
+    check(_lib.load().qlinear_probe_mfma(_ptr(operands), iters, waves_per_simd, _ptr(sink),
+                                         _stream(stream)))
+
+
 def qlinear_gamp_allocate(macs, gain, w_bits: int, budget_bops: int):
     """Host-only: (a_bits list, total BOPs) of the greedy A4->A8 allocation."""
     n = len(macs)

@@ -291,6 +291,35 @@ ql_status qlinear_gemm(qlinear_plan_t p, const void* codes, const float* act_sca
 ql_status qlinear_cfg_combine(const float* Y, int32_t M, int32_t N, float w, float* out,
                               void* stream);
 
+/*
+ * Measurement aid, not a step of the method: the int8 matrix-core rate the
+ * device sustains, reported beside the spec peak as the GEMM's measured
+ * ceiling. One workgroup per compute unit of the current device, with
+ * waves_per_simd waves on each SIMD; every wave loads the same 16 operand
+ * fragments and issues 16 * iters v_mfma_i32_16x16x64_i8 into 16
+ * independent accumulators, successive instructions taking different
+ * fragment pairs (accumulator j multiplies activation-side fragment j % 8
+ * by weight-side fragment (j + j / 8) % 8). No memory access inside the
+ * loop, no barrier, no epilogue. Each thread then writes the int32 sum,
+ * wrapped modulo 2^32, of its accumulator registers.
+ *   operands       : DEVICE int8 [16][64][16]: fragment f (0-7 activation
+ *                    side, 8-15 weight side), lane l, byte i. In the
+ *                    instruction's layout lane l holds row (column) l % 16
+ *                    and the 16 K elements 16 * (l / 16) ... + 15. Random
+ *                    bytes give the rate with operand switching, constant
+ *                    bytes the rate without it.
+ *   iters          : in [0, 2^24].
+ *   waves_per_simd : 1 or 2.
+ *   sink           : DEVICE int32 out [compute units * 256 * waves_per_simd],
+ *                    thread t of workgroup b at b * 256 * waves_per_simd + t.
+ * Total int8 operations of a call: compute units * 4 * waves_per_simd *
+ * iters * 16 * 2 * 16 * 16 * 64.
+ * Errors besides the common ones: QL_ERR_ARG for NULL or misaligned
+ * pointers and out-of-range sizes.
+ */
+ql_status qlinear_probe_mfma(const void* operands, int32_t iters, int32_t waves_per_simd,
+                             int32_t* sink, void* stream);
+
 /* Message for the last non-OK status on this thread ("" if none). */
 const char* qlinear_last_error(void);
 

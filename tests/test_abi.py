@@ -122,6 +122,19 @@ def test_cfg_combine_host_checks():
     assert L.qlinear_cfg_combine(0x1000, 0, 4, 4.0, 0x9000, None) == _lib.QL_OK
 
 
+def test_probe_host_checks():
+    # the MFMA ceiling probe validates its arguments before any device call
+    L = _lib.load()
+    assert L.qlinear_probe_mfma(None, 10, 1, 0x1000, None) == _lib.QL_ERR_ARG
+    assert L.qlinear_probe_mfma(0x1000, 10, 1, None, None) == _lib.QL_ERR_ARG
+    assert L.qlinear_probe_mfma(0x1000, -1, 1, 0x1000, None) == _lib.QL_ERR_ARG
+    assert "iters" in L.qlinear_last_error().decode()
+    assert L.qlinear_probe_mfma(0x1000, 10, 3, 0x1000, None) == _lib.QL_ERR_ARG
+    assert "waves_per_simd" in L.qlinear_last_error().decode()
+    assert L.qlinear_probe_mfma(0x1008, 10, 1, 0x1000, None) == _lib.QL_ERR_ARG
+    assert "aligned" in L.qlinear_last_error().decode()
+
+
 def test_plan_rejects_bad_input_branches():
     def st(offs, **kw):
         arr = (ctypes.c_int32 * len(offs))(*offs)

@@ -591,6 +591,42 @@ def test_one_pass_quantizer_limits_two_branches(torch, K, offs, a_bits, B, x_dty
                    tag=f"one-pass limit M={M}")
 
 
+def _probe_expected(ops: np.ndarray, iters: int) -> int:
+    """Sum, modulo 2^32, of every accumulator of one probe wave: accumulator
+    j adds iters products of fragments (j % 8, 8 + (j + j // 8) % 8); a 16 x
+    16 x 64 product's entries sum to sum_k colsum(A)[k] * rowsum(B)[k], and
+    lane l of a fragment carries row (column) l % 16 and K chunk l // 16."""
+    f = ops.astype(np.int64).reshape(16, 4, 16, 16)   # fragment, K chunk, row/col, byte
+    sums = f.sum(axis=2)                               # [fragment, chunk, byte]: K-indexed sums
+    tot = 0
+    for j in range(16):
+        a, b = j % 8, 8 + (j + j // 8) % 8
+        tot += int((sums[a] * sums[b]).sum())
+    return (tot * iters) % (1 << 32)
+
+
+@pytest.mark.parametrize("kind", ["random", "constant"])
+def test_mfma_probe_sums(torch, kind):
+    # The measurement aid behind the GEMM's measured ceiling: every wave's
+    # accumulators must hold exactly iters times the fragments' products.
+    from bit_post_quantization_amd import qlinear_probe_mfma
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    if kind == "random":
+        ops = np.random.default_rng(7).integers(-128, 128, size=(16, 64, 16), dtype=np.int8)
+    else:
+        ops = np.full((16, 64, 16), 3, np.int8)
+    od = _dev(torch, ops)
+    for wps in (1, 2):
+        for iters in (0, 1, 5, 1000):
+            sink = torch.full((cus * 256 * wps,), -1, dtype=torch.int32, device="cuda")
+            qlinear_probe_mfma(od, iters, wps, sink)
+            torch.cuda.synchronize()
+            per_wave = sink.cpu().numpy().astype(np.int64).reshape(-1, 64).sum(axis=1) % (1 << 32)
+            exp = _probe_expected(ops, iters)
+            assert (per_wave == exp).all(), (kind, wps, iters, per_wave[:4], exp)
+        say(f"[probe] {kind} operands: {cus * 4 * wps} waves, sums exact")
+
+
 def test_static_scales(torch):
     M, K, N = 64, 256, 80
     X = synth.silu_normal(4, "static/X", M, K)
