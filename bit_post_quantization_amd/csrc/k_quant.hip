@@ -212,7 +212,8 @@ __device__ __forceinline__ void scales_from_partials(const QuantArgs& a, int j, 
 // and Q lie strictly on one side of every half-integer and round alike
 // (a Q that rounds onto a half-integer is caught too). Units with a closer
 // value (and non-finite t, or |t| >= 2^21) are redone with the division;
-// that is rare and wave-uniform work is skipped when no lane needs it. Rounding: m = t + 1.5 * 2^23 is t rounded
+// that is rare and wave-uniform work is skipped when no lane needs it.
+// Rounding: m = t + 1.5 * 2^23 is t rounded
 // half to even into the units of [2^23, 2^24) (the sum's even mantissas are
 // the even integers), so m - 1.5 * 2^23 = rint(t) for |t| < 2^22, and after
 // clamping m to 1.5 * 2^23 +- qa the code is the low byte of m's bits (the
@@ -660,7 +661,9 @@ bool run_fused(const QuantArgs& a, hipStream_t s, hipError_t& e) {
       return false;
     const int64_t per = (int64_t)cus * kFThreads;
     const int64_t U = (a.nunits + per - 1) / per;
-    if (U > kFUnits || cus > kMaxReduceBlocks) return false;
+    // workgroup 0 gathers one workgroup's words per thread
+    static_assert(kFThreads <= kMaxReduceBlocks, "exchange words per workgroup");
+    if (U > kFUnits || cus > kFThreads) return false;
     const int G = (int)((a.nunits + U * kFThreads - 1) / (U * kFThreads));
     hipLaunchKernelGGL((k1_fused<BF16, HB, A4, NS>), dim3(G), dim3(kFThreads), 0, s, a, (int)U);
     e = hipGetLastError();
