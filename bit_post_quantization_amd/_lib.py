@@ -68,7 +68,7 @@ def load() -> ctypes.CDLL:
         "qlinear_quantize_act_noalloc": ([P, P, I32, I32, P, P, P, P], ctypes.c_int),
         "qlinear_gemm": ([P, P, P, I32, I32, F32, P, P, P], ctypes.c_int),
         "qlinear_cfg_combine": ([P, I32, I32, F32, P, P], ctypes.c_int),
-        "qlinear_probe_mfma": ([P, I32, I32, P, P], ctypes.c_int),
+        "qlinear_probe_mfma": ([P, I32, I32, P, ctypes.c_int64, P], ctypes.c_int),
         "qlinear_last_error": ([], ctypes.c_char_p),
         "qlinear_version": ([], ctypes.c_char_p),
     }

@@ -615,7 +615,7 @@ ql_status qlinear_gemm(qlinear_plan_t p, const void* codes, const float* act_sca
 }
 
 ql_status qlinear_probe_mfma(const void* operands, int32_t iters, int32_t waves_per_simd,
-                             int32_t* sink, void* stream) {
+                             int32_t* sink, int64_t sink_len, void* stream) {
   if (!operands || !sink) return fail(QL_ERR_ARG, "operands or sink is NULL");
   if (iters < 0 || iters > (1 << 24)) return fail(QL_ERR_ARG, "iters = %d must be in [0, 2^24]", iters);
   if (waves_per_simd != 1 && waves_per_simd != 2)
@@ -626,6 +626,10 @@ ql_status qlinear_probe_mfma(const void* operands, int32_t iters, int32_t waves_
   hipError_t e = hipGetDevice(&dev);
   if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
   if (e != hipSuccess) return hip_fail(e, "querying the compute units");
+  const int64_t need = (int64_t)cus * 256 * waves_per_simd;
+  if (sink_len < need)
+    return fail(QL_ERR_ARG, "sink holds %lld int32, the grid writes %lld", (long long)sink_len,
+                (long long)need);
   e = ql::launch_probe_mfma(operands, iters, waves_per_simd, cus, sink,
                             reinterpret_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "launching the MFMA probe");

@@ -134,7 +134,7 @@ def qlinear_cfg_combine(Y, M: int, N: int, w: float, out, stream=None) -> None:
 def qlinear_probe_mfma(operands, iters: int, waves_per_simd: int, sink, stream=None) -> None:
     """Measurement aid: the int8 MFMA ceiling microkernel (include/qlinear.h)."""
     check(_lib.load().qlinear_probe_mfma(_ptr(operands), iters, waves_per_simd, _ptr(sink),
-                                         _stream(stream)))
+                                         sink.numel(), _stream(stream)))
 
 
 def qlinear_gamp_allocate(macs, gain, w_bits: int, budget_bops: int):

@@ -312,13 +312,15 @@ ql_status qlinear_cfg_combine(const float* Y, int32_t M, int32_t N, float w, flo
  *   waves_per_simd : 1 or 2.
  *   sink           : DEVICE int32 out [compute units * 256 * waves_per_simd],
  *                    thread t of workgroup b at b * 256 * waves_per_simd + t.
+ *   sink_len       : int32 elements of sink; a shorter sink is refused
+ *                    (QL_ERR_ARG) before anything is enqueued.
  * Total int8 operations of a call: compute units * 4 * waves_per_simd *
  * iters * 16 * 2 * 16 * 16 * 64.
  * Errors besides the common ones: QL_ERR_ARG for NULL or misaligned
- * pointers and out-of-range sizes.
+ * pointers, out-of-range sizes and a sink shorter than the grid.
  */
 ql_status qlinear_probe_mfma(const void* operands, int32_t iters, int32_t waves_per_simd,
-                             int32_t* sink, void* stream);
+                             int32_t* sink, int64_t sink_len, void* stream);
 
 /* Message for the last non-OK status on this thread ("" if none). */
 const char* qlinear_last_error(void);

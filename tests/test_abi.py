@@ -125,13 +125,14 @@ def test_cfg_combine_host_checks():
 def test_probe_host_checks():
     # the MFMA ceiling probe validates its arguments before any device call
     L = _lib.load()
-    assert L.qlinear_probe_mfma(None, 10, 1, 0x1000, None) == _lib.QL_ERR_ARG
-    assert L.qlinear_probe_mfma(0x1000, 10, 1, None, None) == _lib.QL_ERR_ARG
-    assert L.qlinear_probe_mfma(0x1000, -1, 1, 0x1000, None) == _lib.QL_ERR_ARG
+    n = 1 << 20
+    assert L.qlinear_probe_mfma(None, 10, 1, 0x1000, n, None) == _lib.QL_ERR_ARG
+    assert L.qlinear_probe_mfma(0x1000, 10, 1, None, n, None) == _lib.QL_ERR_ARG
+    assert L.qlinear_probe_mfma(0x1000, -1, 1, 0x1000, n, None) == _lib.QL_ERR_ARG
     assert "iters" in L.qlinear_last_error().decode()
-    assert L.qlinear_probe_mfma(0x1000, 10, 3, 0x1000, None) == _lib.QL_ERR_ARG
+    assert L.qlinear_probe_mfma(0x1000, 10, 3, 0x1000, n, None) == _lib.QL_ERR_ARG
     assert "waves_per_simd" in L.qlinear_last_error().decode()
-    assert L.qlinear_probe_mfma(0x1008, 10, 1, 0x1000, None) == _lib.QL_ERR_ARG
+    assert L.qlinear_probe_mfma(0x1008, 10, 1, 0x1000, n, None) == _lib.QL_ERR_ARG
     assert "aligned" in L.qlinear_last_error().decode()
 
 

@@ -625,6 +625,11 @@ def test_mfma_probe_sums(torch, kind):
             exp = _probe_expected(ops, iters)
             assert (per_wave == exp).all(), (kind, wps, iters, per_wave[:4], exp)
         say(f"[probe] {kind} operands: {cus * 4 * wps} waves, sums exact")
+    # a sink one element short of the grid is refused before any launch
+    from bit_post_quantization_amd import QLError
+    short = torch.zeros(cus * 256 - 1, dtype=torch.int32, device="cuda")
+    with pytest.raises(QLError, match="sink holds"):
+        qlinear_probe_mfma(od, 1, 1, short)
 
 
 def test_static_scales(torch):
