@@ -246,6 +246,41 @@ __device__ __forceinline__ uint32_t quant_pack(const float (&e)[4], float sp, fl
   return lo | hi;
 }
 
+// quant_pack for scales taken from the tensor's own maxima (s = fl(mx/qa)
+// with every |v| <= mx), so |v/s| <= qa(1 + 2^-23) and no code needs
+// clamping. With r = fl(1/s), the exact product P = v*r is within
+// 2^-23 |q| <= qa 2^-23 (1 + 3u) of the correctly rounded quotient Q (both
+// carry one relative rounding of at most u = 2^-24 from q = v/s).
+// s = fma(v, r, 1.5 * 2^23) rounds P itself half to even into the integers
+// (the code c = s - 1.5 * 2^23, exact, is s's low byte), and
+// e = fma(v, r, -c) = fl(P - c). |e| < lim = 0.5 - (qa + 1) 2^-23 puts P
+// more than qa 2^-23 + 2^-24 from every half-integer, so Q lies strictly
+// between the same two half-integers and rint(Q) = c. Other units (and
+// non-finite products) take the division, as in quant_pack.
+template <bool SYM>
+__device__ __forceinline__ uint32_t quant_pack_own(const float (&e)[4], float sp, float sn, float rp,
+                                                   float rn, float qa, float lim) {
+  constexpr float kMagic = 12582912.0f;  // 1.5 * 2^23
+  float m[4];
+  bool slow = false;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const float v = e[i];
+    const float r = SYM ? rp : (v >= 0.0f ? rp : rn);
+    const float s = fmaf(v, r, kMagic);
+    const float d = fmaf(v, r, -(s - kMagic));
+    slow |= !(fabsf(d) < lim);
+    m[i] = s;
+  }
+  if (slow) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) m[i] = kMagic + (float)quant_dual(e[i], sp, sn, qa);
+  }
+  const uint32_t lo = __builtin_amdgcn_perm(__float_as_uint(m[1]), __float_as_uint(m[0]), 0x0c0c0400u);
+  const uint32_t hi = __builtin_amdgcn_perm(__float_as_uint(m[3]), __float_as_uint(m[2]), 0x04000c0cu);
+  return lo | hi;
+}
+
 // TASQ truncation of a packed unit (k = lsb_k low magnitude bits cleared),
 // then the store: 4 bytes, or (4-bit codes) two bytes of two nibbles each,
 // element 2j in the low nibble of byte j.
@@ -598,6 +633,7 @@ __global__ __launch_bounds__(kFThreads, 1) void k1_fused(QuantArgs a, int U) {
   const __amdgpu_buffer_rsrc_t rc =
       buffer_rsrc(reinterpret_cast<uint8_t*>(a.codes) + first * kCodeBytes, here * kCodeBytes);
   const LsbMask mk(a.keep_mask);
+  const float lim = 0.5f - (a.qa + 1.0f) * 0x1p-23f;  // the scales are the tensor's own
   auto quant_all = [&](auto symc, auto lsbc) __attribute__((always_inline)) {
     constexpr bool SYM = decltype(symc)::value;
     constexpr int LSB = decltype(lsbc)::value ? 1 : 0;
@@ -614,8 +650,14 @@ __global__ __launch_bounds__(kFThreads, 1) void k1_fused(QuantArgs a, int U) {
           rn = b1 ? rns[1] : rn;
           col = step_col(col, cstep, kun);
         }
-        store_unit<A4, LSB>(rc, (uint32_t)(u * kFThreads + tid) * kCodeBytes,
-                            quant_pack<SYM>(e[u], sp, sn, rp, rn, a.qa), mk);
+        // (with the rotation in registers too, the shorter form makes the
+        // compiler spill, so rotated tensors keep quant_pack)
+        uint32_t p;
+        if constexpr (HB == 0)
+          p = quant_pack_own<SYM>(e[u], sp, sn, rp, rn, a.qa, lim);
+        else
+          p = quant_pack<SYM>(e[u], sp, sn, rp, rn, a.qa);
+        store_unit<A4, LSB>(rc, (uint32_t)(u * kFThreads + tid) * kCodeBytes, p, mk);
       }
     }
   };
