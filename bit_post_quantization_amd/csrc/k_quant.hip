@@ -338,6 +338,10 @@ __global__ __launch_bounds__(kThreads) void k1_quantize(QuantArgs a) {
   const int cstep = KS ? kThreads % a.k_units : 0;
   constexpr uint32_t kCodeBytes = A4 ? 2 : 4;
   const LsbMask mk(a.keep_mask);
+  // dynamic scales are the maxima of the very values quantized here
+  // (per branch), so the one-pass kernel's shorter exact test applies
+  const bool own = a.static_scales == nullptr;
+  const float lim = 0.5f - (a.qa + 1.0f) * 0x1p-23f;
   const int64_t nchunks = (a.nunits + kChunk - 1) / kChunk;
   for (int64_t ch = blockIdx.x; ch < nchunks; ch += gridDim.x) {
     float e[kUnroll][4];
@@ -366,8 +370,13 @@ __global__ __launch_bounds__(kThreads) void k1_quantize(QuantArgs a) {
         }
         col = next_col(a, col, cstep);
       }
-      const uint32_t p = a.sym ? quant_pack<true>(e[u], sp, sn, rp, rn, a.qa)
-                               : quant_pack<false>(e[u], sp, sn, rp, rn, a.qa);
+      uint32_t p;
+      if (HB == 0 && own)
+        p = a.sym ? quant_pack_own<true>(e[u], sp, sn, rp, rn, a.qa, lim)
+                  : quant_pack_own<false>(e[u], sp, sn, rp, rn, a.qa, lim);
+      else
+        p = a.sym ? quant_pack<true>(e[u], sp, sn, rp, rn, a.qa)
+                  : quant_pack<false>(e[u], sp, sn, rp, rn, a.qa);
       store_unit<A4>(rc, (uint32_t)(u * kThreads + threadIdx.x) * kCodeBytes, p, mk);
     }
   }
