@@ -65,7 +65,9 @@ def _product_fast(v, s, margin=2.0 ** -22):
     ri = np.rint(t.astype(np.float64))
     d = np.abs(t.astype(np.float64) - ri).astype(f32)
     z = (np.abs(t).astype(np.float64) * margin + d.astype(np.float64)).astype(f32)
-    return ri, (z < f32(0.5 - 2.0 ** -23)) & np.isfinite(t) & (np.abs(t) < 2.0 ** 21)
+    # (non-finite t gives a NaN z, and |t| >= 2^21 a z >= 0.5: both fail)
+    with np.errstate(invalid="ignore"):
+        return ri, z < f32(0.5 - 2.0 ** -23)
 
 
 @pytest.mark.parametrize("qa", [127, 63, 15, 7, 3])
@@ -92,6 +94,11 @@ def test_general_fast_path_matches_division():
         s = np.exp(rng.uniform(-30, 5, n)).astype(f32)  # arbitrary (static) scales
         v = _near_half(rng, n, qa, (s * f32(qa)).astype(f32))
         v2 = (rng.standard_normal(n) * 300).astype(f32) * s  # far beyond the range too
+        v3 = np.concatenate([np.array([np.inf, -np.inf, np.nan], f32),
+                             (np.float32(2.0 ** 21) * s[:1000]).astype(f32),
+                             (np.float32(2.0 ** 23) * s[:1000]).astype(f32)])
+        ri, fast = _product_fast(v3, np.concatenate([s[:3], s[:1000], s[:1000]]))
+        assert not fast.any()  # these always take the division
         for x in (v, v2):
             ri, fast = _product_fast(x, s)
             ref = _reference(x, s, qa)
