@@ -62,11 +62,11 @@ def _product_fast(v, s, margin=2.0 ** -22):
     fl(|t| 2^-22 + |t - rint t|) < 0.5 - 2^-23, then clamped."""
     r = (f32(1) / s).astype(f32)
     t = (v * r).astype(f32)
-    ri = np.rint(t.astype(np.float64))
-    d = np.abs(t.astype(np.float64) - ri).astype(f32)
-    z = (np.abs(t).astype(np.float64) * margin + d.astype(np.float64)).astype(f32)
     # (non-finite t gives a NaN z, and |t| >= 2^21 a z >= 0.5: both fail)
     with np.errstate(invalid="ignore"):
+        ri = np.rint(t.astype(np.float64))
+        d = np.abs(t.astype(np.float64) - ri).astype(f32)
+        z = (np.abs(t).astype(np.float64) * margin + d.astype(np.float64)).astype(f32)
         return ri, z < f32(0.5 - 2.0 ** -23)
 
 
